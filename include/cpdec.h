@@ -1,0 +1,179 @@
+/*
+ * cpdec.h -- context-parallel decode combine on one AMD MI355X (gfx950).
+ *
+ * The operation is the one described on the page "FlashInfer's
+ * Context-Parallel Decode optimisation: Fused A2A + LSE Reduce" (analysis of
+ * flashinfer PR #4929):
+ *   - section "Introduction": the KV cache of every sequence is split along
+ *     the sequence into R shards; decode attention over each shard gives a
+ *     partial output o_r and its log-sum-exp lse_r;
+ *   - section "Code analysis, 1. Fused kernel": the R partials of each
+ *     (sequence, head) are merged with LSE softmax weights, accumulated in
+ *     FP32 and converted to FP16/BF16.
+ * Here all R shards live in one GPU's memory (one GPU's share of the work
+ * after the exchange the page describes); there is no communication.
+ *
+ * Conventions shared by every entry point
+ *   - Plain C ABI.  All tensors are caller-owned device pointers; the library
+ *     never allocates, frees or synchronises, and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     CPDEC_OK means the work was enqueued on that stream; device faults
+ *     surface at the caller's next synchronisation.
+ *   - Every argument check runs before any HIP call; on an error nothing is
+ *     enqueued and the outputs are untouched.  The functions never print,
+ *     abort or throw.
+ *   - Dtypes: CPDEC_F32, CPDEC_F16 (IEEE half), CPDEC_BF16.  Conversions to
+ *     F16/BF16 round to nearest even.
+ *   - Natural logarithms throughout (lse values are ln of sums of e^score).
+ *   - Reentrant and thread-safe; two calls that share a workspace must not
+ *     overlap in time on the device (they would race on it).  The only
+ *     mutable library state is a process-wide counter that tags each call.
+ */
+#ifndef CPDEC_H
+#define CPDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPDEC_MAX_SHARDS 64
+
+typedef enum cpdec_status {
+  CPDEC_OK = 0,
+  CPDEC_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0,
+                                shard count outside [1, CPDEC_MAX_SHARDS],
+                                stride smaller than a row, size overflow    */
+  CPDEC_ERR_UNSUPPORTED = 2, /* head_dim or dtype combination not built    */
+  CPDEC_ERR_ALIGNMENT = 3,   /* pointer or stride not 16-byte aligned       */
+  CPDEC_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned  */
+  CPDEC_ERR_HIP = 5          /* the HIP runtime rejected a kernel launch    */
+} cpdec_status;
+
+typedef enum cpdec_dtype {
+  CPDEC_F32 = 0,
+  CPDEC_F16 = 1,
+  CPDEC_BF16 = 2
+} cpdec_dtype;
+
+/* Shape and layout of one partial-attention call. */
+typedef struct cpdec_attn_desc {
+  int32_t batch;          /* B  > 0: sequences, one query token each        */
+  int32_t num_q_heads;    /* Hq > 0                                          */
+  int32_t num_kv_heads;   /* Hkv > 0, Hq % Hkv == 0; query head hq reads kv
+                             head hq / (Hq / Hkv)                           */
+  int32_t head_dim;       /* D in {64, 128, 256}                             */
+  int32_t num_shards;     /* R in [1, CPDEC_MAX_SHARDS]                      */
+  int32_t kv_capacity;    /* tokens allocated per (shard, sequence, kv head);
+                             every lens entry must be <= kv_capacity        */
+  int64_t kv_stride_batch; /* element strides of each K/V shard tensor;     */
+  int64_t kv_stride_head;  /* the D elements of a token are contiguous.     */
+  int64_t kv_stride_token; /* [B][Hkv][cap][D] contiguous is
+                              (Hkv*cap*D, cap*D, D)                         */
+  float sm_scale;         /* softmax scale; 0 selects 1/sqrt(D)             */
+  cpdec_dtype qkv_dtype;  /* CPDEC_F16 or CPDEC_BF16 (q, K and V)           */
+  cpdec_dtype opart_dtype;/* o_part storage: CPDEC_F32 (recommended), F16,
+                             BF16                                           */
+  int32_t chunk_tokens;   /* split-KV chunk length in tokens; 0 lets the
+                             library pick, otherwise a multiple of 32       */
+} cpdec_attn_desc;
+
+/*
+ * Bytes of device workspace cpdec_attn_partial needs for `d` (0 when every
+ * shard fits one chunk).  Returns 0 for an invalid descriptor as well; such a
+ * descriptor is then rejected by cpdec_attn_partial itself.
+ */
+size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
+
+/*
+ * Per-shard decode attention (page section "Introduction").
+ *
+ * For every shard r, sequence b and query head hq, with L = lens[r*B + b] and
+ * g = hq / (Hq/Hkv):
+ *     s_t    = sm_scale * <q[b,hq,:], K_r[b,g,t,:]>         for t < L
+ *     o_r    = sum_t e^{s_t - m} V_r[b,g,t,:] / sum_t e^{s_t - m},  m = max s
+ *     lse_r  = m + ln sum_t e^{s_t - m}
+ * and an empty shard (L == 0) gives o_r = 0, lse_r = -inf.  Tokens at
+ * positions >= L are never read.
+ *
+ *   d            host pointer to the descriptor (read during the call)
+ *   q            device, [B][Hq][D] contiguous, qkv_dtype, 16-byte aligned
+ *   k_shards     host array of R device pointers; shard r's K is
+ *                [B][Hkv][kv_capacity][D] under the descriptor's strides
+ *   v_shards     same for V (same strides).  Both arrays are read during the
+ *                call and not retained.  Every pointer and every stride (in
+ *                bytes) must be a multiple of 16.
+ *   lens         device, int32 [R][B]; values in [0, kv_capacity] (not
+ *                checked on the device; values outside are undefined behaviour)
+ *   o_part       device, [R][B][Hq][D] contiguous, opart_dtype, 16-byte aligned
+ *   lse_part     device, float [R][B][Hq]
+ *   workspace    device, at least cpdec_attn_workspace_bytes(d) bytes,
+ *                256-byte aligned; may be NULL when that size is 0.  Scratch
+ *                for the split-KV chunk partials and one arrival slot per
+ *                (shard, sequence, kv head, head block).  Its contents on entry
+ *                do not matter (no clearing is needed, also when one buffer
+ *                serves descriptors of different shapes); a call that
+ *                completes leaves every arrival slot at 0.
+ *   stream       hipStream_t
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP (see above).
+ */
+cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
+                                const void* const* k_shards,
+                                const void* const* v_shards,
+                                const int32_t* lens, void* o_part,
+                                float* lse_part, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * LSE merge of R partials (page section "Code analysis, 1. Fused kernel").
+ *
+ * For every row n (a (sequence, head) pair):
+ *     M      = max_r lse_part[r][n]                (over finite entries)
+ *     w_r    = e^{lse_part[r][n] - M}              (shards with -inf skipped:
+ *                                                   their o_part rows are
+ *                                                   never read)
+ *     out[n] = round(sum_r w_r * o_part[r][n][:] / sum_r w_r)
+ *     lse_out[n] = M + ln sum_r w_r
+ * If every shard of a row is -inf: out[n] = 0 and lse_out[n] = -inf.
+ * Weights and the merged lse are formed in FP64, the sum over shards in FP32
+ * in shard order, then one rounding to out_dtype.
+ *
+ *   o_part     device, [R][rows][head_dim] contiguous, in_dtype, 16-byte aligned
+ *   lse_part   device, float [R][rows]; entries finite or -inf (NaN and +inf
+ *              are outside the contract)
+ *   num_shards R in [1, CPDEC_MAX_SHARDS]
+ *   rows       >= 0 (0 enqueues nothing)
+ *   head_dim   in {64, 128, 256, 512}
+ *   in_dtype   CPDEC_F32, CPDEC_F16 or CPDEC_BF16
+ *   out_dtype  CPDEC_F32, CPDEC_F16 or CPDEC_BF16
+ *   out        device, [rows][head_dim], out_dtype, 16-byte aligned
+ *   lse_out    device, float [rows], or NULL to skip writing it
+ *   stream     hipStream_t
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP.
+ */
+cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
+                             int32_t num_shards, int64_t rows, int32_t head_dim,
+                             cpdec_dtype in_dtype, cpdec_dtype out_dtype,
+                             void* out, float* lse_out, void* stream);
+
+/*
+ * Zero-fill `bytes` bytes of a buffer on `stream` with a kernel (no
+ * hipMemset, so it is safe to record in a HIP graph).  Workspaces do not need
+ * it; it is offered for callers that want deterministic buffer contents.
+ * `workspace` must be 256-byte aligned.  Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+cpdec_status cpdec_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* cpdec_status_string(cpdec_status s);
+
+/* Library version string, e.g. "cpdec 0.1.0 gfx950". */
+const char* cpdec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPDEC_H */

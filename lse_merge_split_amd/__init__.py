@@ -1,0 +1,201 @@
+"""cpdec -- context-parallel decode combine on AMD MI355X (gfx950).
+
+Python binding over the C ABI in ``include/cpdec.h`` (libcpdec.so).  It only
+marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+Method: the page "FlashInfer's Context-Parallel Decode optimisation: Fused
+A2A + LSE Reduce" (flashinfer PR #4929) -- per-shard decode attention giving
+(o_r, lse_r) (section "Introduction") and their LSE merge (section "Code
+analysis, 1. Fused kernel").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lib", "AttnDesc", "CpdecError", "attn_partial", "lse_merge", "attn_workspace_bytes",
+           "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpdec.so")
+
+STATUS = {0: "CPDEC_OK", 1: "CPDEC_ERR_INVALID_ARG", 2: "CPDEC_ERR_UNSUPPORTED",
+          3: "CPDEC_ERR_ALIGNMENT", 4: "CPDEC_ERR_WORKSPACE", 5: "CPDEC_ERR_HIP"}
+F32, F16, BF16 = 0, 1, 2
+
+
+class CpdecError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_shards", ctypes.c_int32), ("kv_capacity", ctypes.c_int32),
+                ("kv_stride_batch", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
+                ("kv_stride_token", ctypes.c_int64), ("sm_scale", ctypes.c_float),
+                ("qkv_dtype", ctypes.c_int), ("opart_dtype", ctypes.c_int),
+                ("chunk_tokens", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcpdec.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m lse_merge_split_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.cpdec_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
+        L.cpdec_attn_workspace_bytes.restype = sz
+        L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
+        L.cpdec_attn_partial.restype = ctypes.c_int
+        L.cpdec_lse_merge.argtypes = [vp, vp, i32, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.cpdec_lse_merge.restype = ctypes.c_int
+        L.cpdec_workspace_clear.argtypes = [vp, sz, vp]
+        L.cpdec_workspace_clear.restype = ctypes.c_int
+        L.cpdec_status_string.argtypes = [ctypes.c_int]
+        L.cpdec_status_string.restype = ctypes.c_char_p
+        L.cpdec_version.argtypes = []
+        L.cpdec_version.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+# ------------------------------------------------------------------ torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
+DTYPE_CODES = {"fp32": F32, "fp16": F16, "bf16": BF16}
+
+
+def _stream(t, stream):
+    torch = _torch()
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_attn_desc(q, k_shards, *, kv_capacity=None, sm_scale=0.0, opart_dtype=None,
+                   chunk_tokens=0) -> AttnDesc:
+    """Descriptor from q [B, Hq, D] and K shards [B, Hkv, cap, D] (any strides
+    with a contiguous last dimension; every shard must share them)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    k0 = k_shards[0]
+    _, Hkv, cap, Dk = k0.shape
+    if Dk != D:
+        raise ValueError("head_dim mismatch between q and K")
+    for k in k_shards:
+        if k.shape != k0.shape or k.stride() != k0.stride() or k.stride(-1) != 1:
+            raise ValueError("all K/V shards need one shape and one stride set, D contiguous")
+    d = AttnDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = B, Hq, Hkv, D
+    d.num_shards = len(k_shards)
+    d.kv_capacity = cap if kv_capacity is None else kv_capacity
+    d.kv_stride_batch, d.kv_stride_head, d.kv_stride_token = k0.stride(0), k0.stride(1), k0.stride(2)
+    d.sm_scale = float(sm_scale or 0.0)
+    d.qkv_dtype = dtype_code(q.dtype)
+    d.opart_dtype = dtype_code(opart_dtype if opart_dtype is not None else torch.float32)
+    d.chunk_tokens = int(chunk_tokens)
+    return d
+
+
+def attn_workspace_bytes(desc: AttnDesc) -> int:
+    return int(lib().cpdec_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+_WS_CACHE: dict = {}
+
+
+def _workspace(device, nbytes):
+    """A workspace of at least nbytes, reused across calls and shapes (the
+    library needs no particular contents on entry)."""
+    torch = _torch()
+    key = (str(device),)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def attn_partial(q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
+                 kv_capacity=None, workspace=None, chunk_tokens=0, stream=None):
+    """Per-shard decode attention into o_part [R,B,Hq,D] and lse_part [R,B,Hq].
+
+    lens: int32 device tensor [R, B]."""
+    torch = _torch()
+    if len(k_shards) != len(v_shards):
+        raise ValueError("k_shards and v_shards differ in length")
+    for v, k in zip(v_shards, k_shards):
+        if v.shape != k.shape or v.stride() != k.stride():
+            raise ValueError("V shards must match K shards in shape and strides")
+    if not (q.is_contiguous() and o_part.is_contiguous() and lse_part.is_contiguous()
+            and lens.is_contiguous()):
+        raise ValueError("q, o_part, lse_part and lens must be contiguous")
+    if lens.dtype != torch.int32 or lse_part.dtype != torch.float32:
+        raise TypeError("lens must be int32 and lse_part float32")
+    desc = make_attn_desc(q, k_shards, kv_capacity=kv_capacity, sm_scale=sm_scale,
+                          opart_dtype=o_part.dtype, chunk_tokens=chunk_tokens)
+    R = len(k_shards)
+    if tuple(o_part.shape) != (R, desc.batch, desc.num_q_heads, desc.head_dim):
+        raise ValueError("o_part must be [R, B, Hq, D]")
+    if tuple(lse_part.shape) != (R, desc.batch, desc.num_q_heads) or tuple(lens.shape) != (R, desc.batch):
+        raise ValueError("lse_part must be [R, B, Hq] and lens [R, B]")
+    need = attn_workspace_bytes(desc)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ks = (ctypes.c_void_p * R)(*[k.data_ptr() for k in k_shards])
+    vs = (ctypes.c_void_p * R)(*[v.data_ptr() for v in v_shards])
+    rc = lib().cpdec_attn_partial(ctypes.byref(desc), q.data_ptr(), ks, vs, lens.data_ptr(),
+                                  o_part.data_ptr(), lse_part.data_ptr(), ws_ptr, ws_bytes,
+                                  _stream(q, stream))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_attn_partial")
+
+
+def lse_merge(o_part, lse_part, out, lse_out=None, *, stream=None):
+    """Merge o_part [R, ..., D] with lse_part [R, ...] into out [..., D] and lse_out [...]."""
+    R = o_part.shape[0]
+    D = o_part.shape[-1]
+    rows = o_part.numel() // (R * D)
+    if not (o_part.is_contiguous() and lse_part.is_contiguous() and out.is_contiguous()):
+        raise ValueError("o_part, lse_part and out must be contiguous")
+    if lse_part.numel() != R * rows or out.numel() != rows * D:
+        raise ValueError("shape mismatch between o_part, lse_part and out")
+    if lse_out is not None and (lse_out.numel() != rows or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must hold one value per row")
+    rc = lib().cpdec_lse_merge(o_part.data_ptr(), lse_part.data_ptr(), R, rows, D,
+                               dtype_code(o_part.dtype), dtype_code(out.dtype), out.data_ptr(),
+                               lse_out.data_ptr() if lse_out is not None else None,
+                               _stream(o_part, stream))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_lse_merge")
+
+
+def workspace_clear(ws, *, stream=None):
+    rc = lib().cpdec_workspace_clear(ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream(ws, stream))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_workspace_clear")

@@ -1,0 +1,238 @@
+// cpdec_api.hip -- the C ABI of libcpdec (include/cpdec.h): argument checks,
+// launch planning and kernel dispatch.  Every check runs before any HIP call.
+#include <atomic>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "cpdec.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace cpdec;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int dt) { return dt == CPDEC_F32 || dt == CPDEC_F16 || dt == CPDEC_BF16; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Experiment overrides, read once at first use (never inside a timed loop).
+struct Overrides {
+  int waves = 0;   // CPDEC_WAVES: 1, 2, 4 or 8
+  int chunk = 0;   // CPDEC_CHUNK: tokens, multiple of 32
+  Overrides() {
+    if (const char* s = getenv("CPDEC_WAVES")) {
+      int w = atoi(s);
+      if (w == 1 || w == 2 || w == 4 || w == 8) waves = w;
+    }
+    if (const char* s = getenv("CPDEC_CHUNK")) {
+      int c = atoi(s);
+      if (c >= 32 && c % 32 == 0) chunk = c;
+    }
+  }
+};
+const Overrides& overrides() {
+  static const Overrides o;
+  return o;
+}
+
+constexpr int kDefaultWaves = 4;
+constexpr int kMaxChunkTokens = 2048;   // longest chunk the planner picks
+constexpr int64_t kTargetBlocks = 2048; // workgroups the planner aims for
+
+struct AttnPlan {
+  int waves = 0;
+  int chunk = 0;
+  int nchunks = 0;
+  int G = 0, Gb = 0, gblocks = 0;
+  int64_t units = 0;
+  size_t ws_bytes = 0, off_lse = 0, off_o = 0;
+};
+
+// Validate a descriptor (no pointers) and plan the launch.
+cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
+  if (d == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (d->batch <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->num_shards <= 0 || d->kv_capacity < 0)
+    return CPDEC_ERR_INVALID_ARG;
+  if (d->num_shards > CPDEC_MAX_SHARDS) return CPDEC_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return CPDEC_ERR_INVALID_ARG;
+  if (!(d->sm_scale >= 0.f) || isinf(d->sm_scale)) return CPDEC_ERR_INVALID_ARG;
+  if (d->chunk_tokens < 0 || (d->chunk_tokens > 0 && d->chunk_tokens % kTileTokens != 0))
+    return CPDEC_ERR_INVALID_ARG;
+  const int D = d->head_dim;
+  if (D != 64 && D != 128 && D != 256) return CPDEC_ERR_UNSUPPORTED;
+  if (d->qkv_dtype != CPDEC_F16 && d->qkv_dtype != CPDEC_BF16) return CPDEC_ERR_UNSUPPORTED;
+  if (!valid_dtype(d->opart_dtype)) return CPDEC_ERR_UNSUPPORTED;
+  if (d->kv_stride_token < D || d->kv_stride_head < 0 || d->kv_stride_batch < 0)
+    return CPDEC_ERR_INVALID_ARG;
+  // 16-byte rows: every stride, in bytes, a multiple of 16 (2-byte elements).
+  if ((d->kv_stride_token | d->kv_stride_head | d->kv_stride_batch) % 8 != 0)
+    return CPDEC_ERR_ALIGNMENT;
+
+  AttnPlan p;
+  p.G = d->num_q_heads / d->num_kv_heads;
+  p.Gb = p.G < kGroupRows ? p.G : kGroupRows;
+  p.gblocks = (int)ceil_div(p.G, kGroupRows);
+  p.units = (int64_t)d->num_shards * d->batch * d->num_kv_heads * p.gblocks;
+  p.waves = overrides().waves ? overrides().waves : kDefaultWaves;
+  const int span = kTileTokens * p.waves;  // tokens one pass of all waves covers
+  const int64_t cap = d->kv_capacity > 0 ? d->kv_capacity : 1;
+
+  int chunk = d->chunk_tokens ? d->chunk_tokens : overrides().chunk;
+  if (chunk == 0) {
+    chunk = kMaxChunkTokens;
+    while (chunk > span && p.units * ceil_div(cap, chunk) < kTargetBlocks) chunk /= 2;
+    if (chunk < span) chunk = span;
+    if (chunk > cap) chunk = (int)ceil_div(cap, kTileTokens) * kTileTokens;
+  }
+  if (ceil_div(cap, chunk) > kMaxChunks)
+    chunk = (int)ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
+  p.chunk = chunk;
+  p.nchunks = (int)ceil_div(cap, chunk);
+
+  const int64_t blocks = p.units * p.nchunks;
+  if (blocks > INT32_MAX || (int64_t)d->num_shards * d->batch * d->num_q_heads > INT32_MAX)
+    return CPDEC_ERR_INVALID_ARG;
+
+  if (p.nchunks > 1) {
+    const size_t slots = (size_t)p.units * p.nchunks * p.Gb;
+    p.off_lse = round256((size_t)p.units * sizeof(unsigned long long));
+    p.off_o = p.off_lse + round256(slots * sizeof(float));
+    p.ws_bytes = p.off_o + slots * (size_t)D * sizeof(float);
+  }
+  *pl = p;
+  return CPDEC_OK;
+}
+
+size_t dtype_size(int dt) { return dt == CPDEC_F32 ? 4 : 2; }
+
+// Tags that mark which call an arrival slot belongs to: 48-bit, never 0, a
+// new one per call (a process-wide counter; the only mutable library state).
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> calls{0};
+  unsigned long long t;
+  do {
+    t = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
+  } while (t == 0);
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d) {
+  AttnPlan pl;
+  if (plan_attn(d, &pl) != CPDEC_OK) return 0;
+  return pl.ws_bytes;
+}
+
+cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
+                                const void* const* k_shards, const void* const* v_shards,
+                                const int32_t* lens, void* o_part, float* lse_part,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  AttnPlan pl;
+  cpdec_status st = plan_attn(d, &pl);
+  if (st != CPDEC_OK) return st;
+  if (q == nullptr || k_shards == nullptr || v_shards == nullptr || lens == nullptr ||
+      o_part == nullptr || lse_part == nullptr)
+    return CPDEC_ERR_INVALID_ARG;
+  for (int r = 0; r < d->num_shards; ++r)
+    if (k_shards[r] == nullptr || v_shards[r] == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lens) & 3u))
+    return CPDEC_ERR_ALIGNMENT;
+  for (int r = 0; r < d->num_shards; ++r)
+    if (!aligned16(k_shards[r]) || !aligned16(v_shards[r])) return CPDEC_ERR_ALIGNMENT;
+  if (pl.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.ws_bytes ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return CPDEC_ERR_WORKSPACE;
+  }
+
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  for (int r = 0; r < d->num_shards; ++r) {
+    p.k[r] = k_shards[r];
+    p.v[r] = v_shards[r];
+  }
+  p.lens = lens;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  if (pl.ws_bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    p.ws_cnt = reinterpret_cast<unsigned long long*>(ws);
+    p.ws_lse = reinterpret_cast<float*>(ws + pl.off_lse);
+    p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
+  }
+  p.sb = d->kv_stride_batch;
+  p.sh = d->kv_stride_head;
+  p.st = d->kv_stride_token;
+  p.B = d->batch;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.G = pl.G;
+  p.Gb = pl.Gb;
+  p.gblocks = pl.gblocks;
+  p.R = d->num_shards;
+  p.chunk = pl.chunk;
+  p.nchunks = pl.nchunks;
+  p.odt = d->opart_dtype;
+  const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.tag = next_call_tag();
+
+  hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CPDEC_OK : CPDEC_ERR_HIP;
+}
+
+cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part, int32_t num_shards,
+                             int64_t rows, int32_t head_dim, cpdec_dtype in_dtype,
+                             cpdec_dtype out_dtype, void* out, float* lse_out, void* stream) {
+  if (o_part == nullptr || lse_part == nullptr || out == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (num_shards < 1 || num_shards > CPDEC_MAX_SHARDS || rows < 0) return CPDEC_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return CPDEC_ERR_UNSUPPORTED;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return CPDEC_ERR_UNSUPPORTED;
+  if (!aligned16(o_part) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_out) & 3u))
+    return CPDEC_ERR_ALIGNMENT;
+  // Element counts must stay addressable and the grid within 2^31 blocks.
+  if (rows > 0 && (uint64_t)rows * (uint64_t)num_shards > (uint64_t)INT64_MAX / 4096)
+    return CPDEC_ERR_INVALID_ARG;
+  if (lse_merge_max_blocks(rows, head_dim, in_dtype) > INT32_MAX) return CPDEC_ERR_INVALID_ARG;
+  (void)dtype_size;
+  if (rows == 0) return CPDEC_OK;
+  hipError_t e = launch_lse_merge(o_part, lse_part, num_shards, rows, head_dim, in_dtype,
+                                  out_dtype, out, lse_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CPDEC_OK : CPDEC_ERR_HIP;
+}
+
+cpdec_status cpdec_workspace_clear(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return CPDEC_OK;
+  if (workspace == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return CPDEC_ERR_ALIGNMENT;
+  hipError_t e = launch_clear(workspace, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CPDEC_OK : CPDEC_ERR_HIP;
+}
+
+const char* cpdec_status_string(cpdec_status s) {
+  switch (s) {
+    case CPDEC_OK: return "CPDEC_OK";
+    case CPDEC_ERR_INVALID_ARG: return "CPDEC_ERR_INVALID_ARG";
+    case CPDEC_ERR_UNSUPPORTED: return "CPDEC_ERR_UNSUPPORTED";
+    case CPDEC_ERR_ALIGNMENT: return "CPDEC_ERR_ALIGNMENT";
+    case CPDEC_ERR_WORKSPACE: return "CPDEC_ERR_WORKSPACE";
+    case CPDEC_ERR_HIP: return "CPDEC_ERR_HIP";
+  }
+  return "CPDEC_ERR_UNKNOWN";
+}
+
+const char* cpdec_version(void) { return "cpdec 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// device_common.h -- small device helpers shared by the cpdec kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpdec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Storage tags: 16-bit element types are handled as raw bits.
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// ---- 16-bit <-> fp32 conversions ------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <typename T> __device__ __forceinline__ float lo_of(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi_of(uint32_t w);
+template <> __device__ __forceinline__ float lo_of<bf16_t>(uint32_t w) { return bf16_lo(w); }
+template <> __device__ __forceinline__ float hi_of<bf16_t>(uint32_t w) { return bf16_hi(w); }
+template <> __device__ __forceinline__ float lo_of<f16_t>(uint32_t w) { return f16_lo(w); }
+template <> __device__ __forceinline__ float hi_of<f16_t>(uint32_t w) { return f16_hi(w); }
+
+// Two fp32 values -> one dword holding two 16-bit values (round to nearest
+// even), element a in the low half.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// ---- MFMA: D(16x16 f32) += A(16x32) * B(32x16) -----------------------------
+// Operand layout (64 lanes): lane l supplies A[l % 16][8*(l/16) + j] and
+// B[8*(l/16) + j][l % 16] for j = 0..7 (8 packed 16-bit values, j = 0 in the
+// low half of the first dword); it receives D[4*(l/16) + i][l % 16], i = 0..3.
+template <typename T> __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mfma16x16x32<bf16_t>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma16x16x32<f16_t>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Byte permute of the 8-byte value {hi:lo}: selector byte i picks result byte i.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+constexpr uint32_t kSelLoHalves = 0x05040100u;  // {lo16(hi), lo16(lo)}
+constexpr uint32_t kSelHiHalves = 0x07060302u;  // {hi16(hi), hi16(lo)}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace cpdec

@@ -1,0 +1,43 @@
+// kernels.h -- internal launch interface between the C-ABI host code and the
+// HIP kernels of libcpdec.  Not installed; the public API is include/cpdec.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpdec {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+constexpr int kMaxShards = 64;     // equals CPDEC_MAX_SHARDS
+constexpr int kTileTokens = 32;    // tokens one wave consumes per loop step
+constexpr int kMaxChunks = 256;    // split-KV chunks per (shard, seq, kv head)
+constexpr int kGroupRows = 16;     // query heads per MFMA column block
+
+struct AttnParams {
+  const void* q;
+  const void* k[kMaxShards];
+  const void* v[kMaxShards];
+  const int32_t* lens;
+  void* o_part;
+  float* lse_part;
+  float* ws_o;        // [units][nchunks][Gb][D] chunk partials (normalised)
+  float* ws_lse;      // [units][nchunks][Gb]    chunk lse (natural log)
+  unsigned long long* ws_cnt;  // [units] arrival slots: (call tag << 16) | count
+  int64_t sb, sh, st; // K/V element strides: batch, head, token
+  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, odt;
+  float scale_log2;   // sm_scale * log2(e)
+  unsigned long long tag;  // per-call tag, 1 .. 2^48-1
+};
+
+// Launch the partial-attention kernel over units x nchunks workgroups.
+hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
+                               int64_t units, hipStream_t s);
+
+hipError_t launch_lse_merge(const void* o, const float* lse, int R, int64_t rows, int D,
+                            int in_dt, int out_dt, void* out, float* lse_out, hipStream_t s);
+int64_t lse_merge_max_blocks(int64_t rows, int D, int in_dt);
+
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace cpdec

@@ -1,0 +1,209 @@
+// lse_merge.hip -- fused LSE merge of R partial outputs (gfx950).
+//
+// Method: page "FlashInfer's Context-Parallel Decode optimisation: Fused A2A
+// + LSE Reduce" (flashinfer PR #4929), section "Code analysis, 1. Fused
+// kernel": each output row is the sum over shards of o_r weighted by
+// e^{lse_r - max lse}, divided by the sum of the weights, accumulated in FP32
+// and converted to FP16/BF16; the merged lse is max lse + ln(sum of weights).
+//
+// Design (HBM-streaming, ~0.5 flop/byte, no MFMA):
+//   * One row group of GS lanes per output row; each lane owns 16-byte
+//     vectors of the row (D=512 bf16: one wave per row, one 16-byte load per
+//     lane per shard; D=128 fp32: two rows per wave).
+//   * Weights are formed in FP64 (one exp per shard) so the merged lse keeps
+//     ~1e-7 relative accuracy even when it cancels towards 0; the o sum is FP32
+//     in shard order and the division by the weight sum is applied once at the
+//     end.
+//   * Shards with lse = -inf are skipped before their row is loaded: their
+//     bytes are never read and any garbage/NaN in them cannot leak.
+//   * Loads of a batch of 8 shards are issued back to back before any use so
+//     8 x 16 bytes per lane are in flight.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cpdec {
+namespace {
+
+template <typename T> struct InVec;
+template <> struct InVec<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void cvt(u32x4 w, float* x) {
+    x[0] = __uint_as_float(w[0]); x[1] = __uint_as_float(w[1]);
+    x[2] = __uint_as_float(w[2]); x[3] = __uint_as_float(w[3]);
+  }
+};
+template <typename T16> struct InVec16 {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void cvt(u32x4 w, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[2 * i] = lo_of<T16>(w[i]); x[2 * i + 1] = hi_of<T16>(w[i]); }
+  }
+};
+template <> struct InVec<bf16_t> : InVec16<bf16_t> {};
+template <> struct InVec<f16_t> : InVec16<f16_t> {};
+
+// Store N floats (N = 4 or 8) as Tout.
+template <typename Tout, int N> __device__ __forceinline__ void store_vec(Tout* p, const float* x);
+template <> __device__ __forceinline__ void store_vec<float, 4>(float* p, const float* x) {
+  f32x4 v = {x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store_vec<float, 8>(float* p, const float* x) {
+  store_vec<float, 4>(p, x);
+  store_vec<float, 4>(p + 4, x + 4);
+}
+template <typename T16, int N> __device__ __forceinline__ void store_vec16(T16* p, const float* x) {
+  if constexpr (N == 8) {
+    u32x4 v = {pack2<T16>(x[0], x[1]), pack2<T16>(x[2], x[3]), pack2<T16>(x[4], x[5]),
+               pack2<T16>(x[6], x[7])};
+    st16(p, v);
+  } else {
+    u32x2 v = {pack2<T16>(x[0], x[1]), pack2<T16>(x[2], x[3])};
+    *reinterpret_cast<u32x2*>(p) = v;
+  }
+}
+template <> __device__ __forceinline__ void store_vec<bf16_t, 4>(bf16_t* p, const float* x) { store_vec16<bf16_t, 4>(p, x); }
+template <> __device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* p, const float* x) { store_vec16<bf16_t, 8>(p, x); }
+template <> __device__ __forceinline__ void store_vec<f16_t, 4>(f16_t* p, const float* x) { store_vec16<f16_t, 4>(p, x); }
+template <> __device__ __forceinline__ void store_vec<f16_t, 8>(f16_t* p, const float* x) { store_vec16<f16_t, 8>(p, x); }
+
+constexpr int kMergeWaves = 4;
+constexpr int kBatch = 8;  // shards whose loads are in flight together
+
+template <typename Tin, typename Tout, int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
+    const Tin* __restrict__ o, const float* __restrict__ lse, int R, int64_t rows,
+    Tout* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int VEC = InVec<Tin>::N;       // elements per 16-byte load
+  constexpr int NV = D / VEC;              // 16-byte vectors per row
+  constexpr int GS = NV < 64 ? NV : 64;    // lanes per row
+  constexpr int RPW = 64 / GS;             // rows per wave
+  constexpr int VPL = NV / GS;             // vectors per lane
+  static_assert(NV % GS == 0 && 64 % GS == 0, "row split");
+
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW + lane / GS;
+  const int li = lane % GS;
+  if (row >= rows) return;
+
+  const float* lrow = lse + row;
+  float M = neg_inf();
+  for (int r = 0; r < R; ++r) M = fmaxf(M, lrow[(int64_t)r * rows]);
+
+  Tout* orow = out + row * D;
+  if (M == neg_inf()) {  // every shard empty: out = 0, lse = -inf
+    float z[VEC] = {};
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, z);
+    if (lse_out != nullptr && li == 0) lse_out[row] = neg_inf();
+    return;
+  }
+
+  const double Md = (double)M;
+  double S = 0.0;
+  float acc[VPL][VEC];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[v][e] = 0.f;
+
+  const Tin* obase = o + row * D + li * VEC;
+  for (int rb = 0; rb < R; rb += kBatch) {
+    float lb[kBatch];
+    u32x4 raw[kBatch][VPL];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int r = rb + j;
+      lb[j] = (r < R) ? lrow[(int64_t)r * rows] : neg_inf();
+      if (lb[j] != neg_inf()) {
+        const Tin* src = obase + (int64_t)r * rows * D;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(src + v * GS * VEC);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (lb[j] == neg_inf()) continue;  // empty shard: skipped, never read
+      const double e = exp((double)lb[j] - Md);
+      S += e;
+      const float w = (float)e;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        float x[VEC];
+        InVec<Tin>::cvt(raw[j][v], x);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(w, x[k], acc[v][k]);
+      }
+    }
+  }
+
+  const float inv = (float)(1.0 / S);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    float y[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) y[k] = acc[v][k] * inv;
+    store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, y);
+  }
+  if (lse_out != nullptr && li == 0) lse_out[row] = (float)(Md + log(S));
+}
+
+template <typename Tin, typename Tout, int D>
+hipError_t launch_typed(const void* o, const float* lse, int R, int64_t rows, void* out,
+                        float* lse_out, hipStream_t s) {
+  constexpr int VEC = InVec<Tin>::N;
+  constexpr int NV = D / VEC;
+  constexpr int GS = NV < 64 ? NV : 64;
+  constexpr int rows_per_block = kMergeWaves * (64 / GS);
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D>), dim3((unsigned)blocks),
+                     dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
+                     static_cast<Tout*>(out), lse_out);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_d(const void* o, const float* lse, int R, int64_t rows, int D, void* out,
+                    float* lse_out, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_typed<Tin, Tout, 64>(o, lse, R, rows, out, lse_out, s);
+    case 128: return launch_typed<Tin, Tout, 128>(o, lse, R, rows, out, lse_out, s);
+    case 256: return launch_typed<Tin, Tout, 256>(o, lse, R, rows, out, lse_out, s);
+    case 512: return launch_typed<Tin, Tout, 512>(o, lse, R, rows, out, lse_out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename Tin>
+hipError_t launch_out(const void* o, const float* lse, int R, int64_t rows, int D, int out_dt,
+                      void* out, float* lse_out, hipStream_t s) {
+  switch (out_dt) {
+    case kF32: return launch_d<Tin, float>(o, lse, R, rows, D, out, lse_out, s);
+    case kF16: return launch_d<Tin, f16_t>(o, lse, R, rows, D, out, lse_out, s);
+    case kBF16: return launch_d<Tin, bf16_t>(o, lse, R, rows, D, out, lse_out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int64_t lse_merge_max_blocks(int64_t rows, int D, int in_dt) {
+  const int vec = in_dt == kF32 ? 4 : 8;
+  const int nv = D / vec;
+  const int gs = nv < 64 ? nv : 64;
+  const int rows_per_block = kMergeWaves * (64 / gs);
+  return (rows + rows_per_block - 1) / rows_per_block;
+}
+
+hipError_t launch_lse_merge(const void* o, const float* lse, int R, int64_t rows, int D,
+                            int in_dt, int out_dt, void* out, float* lse_out, hipStream_t s) {
+  switch (in_dt) {
+    case kF32: return launch_out<float>(o, lse, R, rows, D, out_dt, out, lse_out, s);
+    case kF16: return launch_out<f16_t>(o, lse, R, rows, D, out_dt, out, lse_out, s);
+    case kBF16: return launch_out<bf16_t>(o, lse, R, rows, D, out_dt, out, lse_out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpdec

@@ -1,0 +1,157 @@
+"""The C ABI on a CPU host: the library loads, exports every function that
+include/cpdec.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lse_merge_split_amd as cp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, ALIGN, WS = 0, 1, 2, 3, 4
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "cpdec.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpdec_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = cp.lib()
+    names = _declared()
+    assert {"cpdec_attn_partial", "cpdec_lse_merge", "cpdec_attn_workspace_bytes",
+            "cpdec_workspace_clear", "cpdec_status_string", "cpdec_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = cp.lib()
+    for code, name in cp.STATUS.items():
+        assert lib.cpdec_status_string(code).decode() == name
+    assert lib.cpdec_status_string(99).decode() == "CPDEC_ERR_UNKNOWN"
+    assert b"gfx950" in lib.cpdec_version()
+
+
+def _desc(**kw):
+    d = cp.AttnDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim, d.num_shards = 2, 8, 2, 128, 4
+    d.kv_capacity = 1000
+    d.kv_stride_token, d.kv_stride_head = 128, 1000 * 128
+    d.kv_stride_batch = 2 * 1000 * 128
+    d.sm_scale, d.qkv_dtype, d.opart_dtype, d.chunk_tokens = 0.0, cp.BF16, cp.F32, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_bytes():
+    lib = cp.lib()
+    one = _desc(chunk_tokens=1024)   # a single chunk covers the capacity
+    assert lib.cpdec_attn_workspace_bytes(ctypes.byref(one)) == 0
+    split = _desc(chunk_tokens=128)  # 8 chunks -> counters + partials
+    nb = lib.cpdec_attn_workspace_bytes(ctypes.byref(split))
+    units, nch, Gb, D = 4 * 2 * 2, 8, 4, 128
+    assert nb >= units * nch * Gb * (D + 1) * 4 + units * 4
+    assert lib.cpdec_attn_workspace_bytes(None) == 0
+    assert lib.cpdec_attn_workspace_bytes(ctypes.byref(_desc(head_dim=96))) == 0
+
+
+# Fake (never dereferenced) device addresses.  Every call below must fail
+# validation, which runs before any HIP call; with a GPU visible a wrong
+# acceptance would launch a kernel on these addresses, so the cases run only
+# on hosts without a GPU.
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+needs_cpu_host = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer cases run on GPU-less hosts")
+A = 1 << 20  # aligned fake address
+
+
+def _attn(d, q=A, k=A, v=A, lens=A, o=A, lse=A, ws=None, wsb=0, R=None):
+    if R is None and d is not None:
+        R = max(d.num_shards, 1)
+    R = 1 if d is None else R
+    ks = (ctypes.c_void_p * max(R, 1))(*([k] * max(R, 1)))
+    vs = (ctypes.c_void_p * max(R, 1))(*([v] * max(R, 1)))
+    return cp.lib().cpdec_attn_partial(ctypes.byref(d) if d is not None else None, q, ks, vs,
+                                       lens, o, lse, ws, wsb, None)
+
+
+@needs_cpu_host
+@pytest.mark.parametrize("case,code", [
+    (dict(batch=0), INVALID), (dict(num_q_heads=7), INVALID), (dict(num_kv_heads=0), INVALID),
+    (dict(num_shards=0), INVALID), (dict(num_shards=65), INVALID), (dict(kv_capacity=-1), INVALID),
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=512), UNSUPPORTED),
+    (dict(qkv_dtype=cp.F32), UNSUPPORTED), (dict(opart_dtype=7), UNSUPPORTED),
+    (dict(kv_stride_token=64), INVALID), (dict(kv_stride_token=132), ALIGN),
+    (dict(kv_stride_head=1000 * 128 + 4), ALIGN), (dict(chunk_tokens=100), INVALID),
+    (dict(sm_scale=-1.0), INVALID), (dict(sm_scale=float("inf")), INVALID),
+])
+def test_attn_descriptor_errors(case, code):
+    kw = dict(chunk_tokens=1024)
+    kw.update(case)
+    assert _attn(_desc(**kw)) == code
+
+
+@needs_cpu_host
+def test_attn_pointer_errors():
+    d = _desc(chunk_tokens=1024)
+    assert _attn(None) == INVALID
+    assert _attn(d, q=None) == INVALID
+    assert _attn(d, k=None) == INVALID
+    assert _attn(d, lens=None) == INVALID
+    assert _attn(d, o=None) == INVALID
+    assert _attn(d, lse=None) == INVALID
+    assert _attn(d, q=A + 8) == ALIGN
+    assert _attn(d, k=A + 2) == ALIGN
+    assert _attn(d, v=A + 4) == ALIGN
+    assert _attn(d, o=A + 4) == ALIGN
+    assert _attn(d, lse=A + 2) == ALIGN
+    split = _desc(chunk_tokens=128)
+    need = cp.lib().cpdec_attn_workspace_bytes(ctypes.byref(split))
+    assert _attn(split) == WS
+    assert _attn(split, ws=A, wsb=need - 1) == WS
+    assert _attn(split, ws=A + 16, wsb=need) == WS
+
+
+@needs_cpu_host
+def test_merge_errors():
+    m = cp.lib().cpdec_lse_merge
+    assert m(None, A, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
+    assert m(A, None, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
+    assert m(A, A, 4, 10, 128, cp.BF16, cp.BF16, None, A, None) == INVALID
+    assert m(A, A, 0, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
+    assert m(A, A, 65, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
+    assert m(A, A, 4, -1, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
+    assert m(A, A, 4, 10, 96, cp.BF16, cp.BF16, A, A, None) == UNSUPPORTED
+    assert m(A, A, 4, 10, 1024, cp.BF16, cp.BF16, A, A, None) == UNSUPPORTED
+    assert m(A, A, 4, 10, 128, 5, cp.BF16, A, A, None) == UNSUPPORTED
+    assert m(A, A, 4, 10, 128, cp.BF16, 9, A, A, None) == UNSUPPORTED
+    assert m(A + 8, A, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == ALIGN
+    assert m(A, A, 4, 10, 128, cp.BF16, cp.BF16, A + 8, A, None) == ALIGN
+    assert m(A, A + 2, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == ALIGN
+    assert m(A, A, 4, 10, 128, cp.BF16, cp.BF16, A, A + 1, None) == ALIGN
+    assert m(A, A, 4, 0, 128, cp.BF16, cp.BF16, A, None, None) == OK  # nothing enqueued
+
+
+@needs_cpu_host
+def test_workspace_clear_errors():
+    c = cp.lib().cpdec_workspace_clear
+    assert c(None, 0, None) == OK
+    assert c(None, 256, None) == INVALID
+    assert c(A + 16, 256, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(cp, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(cp, "_LIB", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        cp.lib()

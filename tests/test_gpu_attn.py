@@ -1,0 +1,264 @@
+"""GPU parity of cpdec_attn_partial (+ cpdec_lse_merge) against the oracle.
+
+Small workloads are compared element by element on every output; the three
+large workloads are run at full size in the launch configuration the
+benchmark uses and compared on sampled (sequence, kv head) groups, with
+properties checked on every row.  Each case prints its name (flushed) first.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import workloads as ow
+from synth import configs as sc
+from tests.helpers import assert_lse, assert_out, run_path, to64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import lse_merge_split_amd as cp  # noqa: E402
+from synth import gpu as sg  # noqa: E402
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check_groups(w, inp, res, groups, o_part_check=True):
+    """Compare the GPU results of the listed (b, h) groups with the oracle."""
+    lens = inp["lens_np"]
+    G = w.G
+    for (b, h) in groups:
+        ref = ow.group(w, lens, b, h)
+        heads = slice(h * G, (h + 1) * G)
+        assert_out(to64(res["out"][b, heads]), ref["out"], f"out b={b} h={h}")
+        if res["lse_out"] is not None:
+            assert_lse(to64(res["lse_out"][b, heads]), ref["lse_out"], f"lse_out b={b} h={h}")
+        if o_part_check:
+            assert_out(to64(res["o_part"][:, b, heads]), ref["o_part"], f"o_part b={b} h={h}")
+            assert_lse(to64(res["lse_part"][:, b, heads]), ref["lse_part"], f"lse_part b={b} h={h}",
+                       floor=True)
+
+
+def all_groups(w):
+    return [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+
+
+SMALL = {
+    "c1": sc.WORKLOADS["c1"],
+    "c2": sc.WORKLOADS["c2"],
+    "c3_small": sc.small("c3", B=2, Lcap=1024, L=1000),
+    "c4_small": sc.small("c4", B=16, Lcap=512),
+    "d256_g20": sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290),
+    "fp16_g8": sc.small("c4", B=4, Lcap=256, dtype="fp16"),
+    "d64_g3": sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attn_small_all_outputs(name):
+    w = SMALL[name]
+    _say(f"attn small {name}")
+    inp = sg.attn_inputs(w)
+    res = run_path(inp)
+    check_groups(w, inp, res, all_groups(w))
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128, 256, 2048])
+def test_attn_chunk_sizes(chunk):
+    """Forced chunk lengths exercise the intra-workgroup merge with idle waves
+    and the last-arrival chunk merge."""
+    w = SMALL["c4_small"]
+    _say(f"attn chunk {chunk}")
+    inp = sg.attn_inputs(w)
+    res = run_path(inp, chunk_tokens=chunk)
+    check_groups(w, inp, res, all_groups(w))
+
+
+@pytest.mark.parametrize("o_dt", ["bf16", "fp16"])
+def test_attn_low_precision_partials(o_dt):
+    """o_part stored in 16 bits: each partial within its own rounding of the
+    oracle's partial (2^-8 relative for bf16) -- the merged output is not held
+    to the fp32-partial bar here."""
+    w = SMALL["c3_small"]
+    _say(f"attn o_part {o_dt}")
+    inp = sg.attn_inputs(w)
+    res = run_path(inp, o_dtype=sg.torch_dtype(o_dt))
+    for (b, h) in all_groups(w):
+        ref = ow.group(w, inp["lens_np"], b, h)
+        heads = slice(h * w.G, (h + 1) * w.G)
+        got = to64(res["o_part"][:, b, heads])
+        assert np.all(np.abs(got - ref["o_part"]) <= 2.0 ** -8 * np.abs(ref["o_part"]) + 1e-3)
+
+
+def test_attn_padding_is_never_read():
+    """NaN in every token position >= L changes no output bit."""
+    w = SMALL["c4_small"]
+    _say("attn NaN padding")
+    clean = run_path(sg.attn_inputs(w))
+    poisoned = run_path(sg.attn_inputs(w, poison_padding=True))
+    for key in ("o_part", "lse_part", "out", "lse_out"):
+        assert torch.equal(clean[key], poisoned[key]), key
+
+
+def test_attn_workspace_reuse_and_determinism():
+    """Two calls on one workspace give identical bits (the arrival counters
+    are left at zero)."""
+    w = SMALL["c3_small"]
+    _say("attn workspace reuse")
+    inp = sg.attn_inputs(w)
+    desc = cp.make_attn_desc(inp["q"], inp["k_shards"], chunk_tokens=128)
+    ws = torch.zeros(cp.attn_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    a = run_path(inp, chunk_tokens=128, workspace=ws)
+    b = run_path(inp, chunk_tokens=128, workspace=ws)
+    units = w.R * w.B * w.Hkv            # one 8-byte arrival slot per unit
+    assert torch.count_nonzero(ws[:8 * units]).item() == 0
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_attn_workspace_contents_do_not_matter():
+    """A workspace full of random bytes, or one last used by a different
+    shape, gives the same bits as a fresh one."""
+    w = SMALL["c4_small"]
+    _say("attn garbage / cross-shape workspace")
+    inp = sg.attn_inputs(w)
+    desc = cp.make_attn_desc(inp["q"], inp["k_shards"], chunk_tokens=64)
+    nb = cp.attn_workspace_bytes(desc)
+    ws = torch.zeros(nb + (1 << 20), dtype=torch.uint8, device="cuda")
+    ref = run_path(inp, chunk_tokens=64, workspace=ws)
+    ws.random_(0, 256)
+    got = run_path(inp, chunk_tokens=64, workspace=ws)
+    for key in ref:
+        assert torch.equal(ref[key], got[key]), key
+    # another shape writes its partials over this shape's slot region, then back
+    w2 = sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290)
+    other = sg.attn_inputs(w2)
+    run_path(other, chunk_tokens=32, workspace=ws)
+    again = run_path(inp, chunk_tokens=64, workspace=ws)
+    for key in ref:
+        assert torch.equal(ref[key], again[key]), key
+    check_groups(w, inp, again, all_groups(w))
+
+
+def test_attn_strided_token_major_layout():
+    """K/V stored token-major ([B][cap][Hkv][D]) give the same bits as the
+    head-major layout (strides passed through the descriptor)."""
+    w = SMALL["c3_small"]
+    _say("attn NHD strides")
+    inp = sg.attn_inputs(w)
+    base = run_path(inp)
+    k_nhd = inp["k"].permute(0, 1, 3, 2, 4).contiguous()   # [R][B][cap][Hkv][D]
+    v_nhd = inp["v"].permute(0, 1, 3, 2, 4).contiguous()
+    inp2 = dict(inp)
+    inp2["k_shards"] = [k_nhd[r].permute(0, 2, 1, 3) for r in range(w.R)]
+    inp2["v_shards"] = [v_nhd[r].permute(0, 2, 1, 3) for r in range(w.R)]
+    assert inp2["k_shards"][0].stride(2) == w.Hkv * w.D
+    res = run_path(inp2)
+    for key in base:
+        assert torch.equal(base[key], res[key]), key
+
+
+def test_attn_empty_shards_and_all_empty_sequence():
+    """An empty shard yields (0, -inf); a sequence whose shards are all empty
+    yields out = 0, lse = -inf; inserting an empty shard changes no bit of the
+    merged result."""
+    w = sc.small("c4", B=3, Lcap=200, Hq=16, Hkv=4, R=3)
+    _say("attn empty shards")
+    inp = sg.attn_inputs(w)
+    lens = inp["lens_np"].copy()
+    lens[:, 1] = 0            # sequence 1: every shard empty
+    lens[2, 0] = 0            # one empty shard of sequence 0
+    lens[0, 2] = 200
+    inp["lens_np"] = lens
+    inp["lens"] = torch.from_numpy(lens).cuda()
+    res = run_path(inp, chunk_tokens=128)
+    check_groups(w, inp, res, all_groups(w))
+    assert torch.count_nonzero(res["out"][1]).item() == 0
+    assert torch.isneginf(res["lse_out"][1]).all()
+    assert torch.count_nonzero(res["o_part"][2, 0]).item() == 0
+    assert torch.isneginf(res["lse_part"][2, 0]).all()
+    # insert an empty 4th shard (length 0): merged outputs unchanged bit for bit
+    inp4 = dict(inp)
+    inp4["k_shards"] = inp["k_shards"] + [inp["k_shards"][0]]
+    inp4["v_shards"] = inp["v_shards"] + [inp["v_shards"][0]]
+    lens4 = np.concatenate([lens, np.zeros((1, w.B), np.int32)])
+    inp4["lens"] = torch.from_numpy(lens4).cuda()
+    res4 = run_path(inp4, chunk_tokens=128)
+    assert torch.equal(res4["out"], res["out"]) and torch.equal(res4["lse_out"], res["lse_out"])
+
+
+def test_attn_split_invariance_on_gpu():
+    """One KV sequence cut into shards gives the result of the unsplit
+    sequence (R=1, L = sum of lengths), within the output tolerance."""
+    w = sc.small("c3", R=1, B=2, Hq=8, Hkv=2, Lcap=1500, L=1500)
+    _say("attn split invariance")
+    inp = sg.attn_inputs(w)
+    whole = run_path(inp)
+    cuts = [0, 1, 200, 777, 1500]          # shards of length 1, 199, 577, 723
+    ks = [inp["k"][0][:, :, a:b] for a, b in zip(cuts[:-1], cuts[1:])]
+    vs = [inp["v"][0][:, :, a:b] for a, b in zip(cuts[:-1], cuts[1:])]
+    Lmax = max(b - a for a, b in zip(cuts[:-1], cuts[1:]))
+    kpad = torch.zeros((4, w.B, w.Hkv, Lmax, w.D), dtype=inp["k"].dtype, device="cuda")
+    vpad = torch.zeros_like(kpad)
+    for r in range(4):
+        kpad[r, :, :, :ks[r].shape[2]] = ks[r]
+        vpad[r, :, :, :vs[r].shape[2]] = vs[r]
+    lens = np.array([[b - a] * w.B for a, b in zip(cuts[:-1], cuts[1:])], np.int32)
+    split = run_path(dict(q=inp["q"], k_shards=[kpad[r] for r in range(4)],
+                          v_shards=[vpad[r] for r in range(4)], lens=torch.from_numpy(lens).cuda()))
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = ow.group(w, inp["lens_np"], b, h)  # oracle of the unsplit sequence
+            heads = slice(h * w.G, (h + 1) * w.G)
+            assert_out(to64(split["out"][b, heads]), ref["out"])
+            assert_lse(to64(split["lse_out"][b, heads]), ref["lse_out"])
+            assert_out(to64(whole["out"][b, heads]), ref["out"])
+
+
+# ------------------------------------------------------------------ full sizes
+def _full(name, groups_fn):
+    w = sc.WORKLOADS[name]
+    _say(f"attn full {name}: allocating and filling inputs")
+    inp = sg.attn_inputs(w)
+    torch.cuda.synchronize()
+    _say(f"attn full {name}: running")
+    res = run_path(inp)
+    lens = inp["lens_np"]
+    # properties on every row
+    lse_out = to64(res["lse_out"])
+    lse_part = to64(res["lse_part"])
+    assert torch.isfinite(res["out"].float()).all()
+    live = np.repeat(lens[:, :, None] > 0, w.Hq, axis=2)        # [R,B,Hq]
+    assert np.array_equal(np.isneginf(lse_part), ~live)
+    anylive = live.any(axis=0)
+    assert np.array_equal(np.isneginf(lse_out), ~anylive)
+    Mx = np.where(live, lse_part, -np.inf).max(axis=0)
+    nl = live.sum(axis=0)
+    assert np.all(lse_out[anylive] >= Mx[anylive] - 1e-5 * np.abs(Mx[anylive]))
+    assert np.all(lse_out[anylive] <= Mx[anylive] + np.log(nl[anylive]) + 1e-5 * np.abs(Mx[anylive]))
+    _say(f"attn full {name}: oracle on sampled groups")
+    check_groups(w, inp, res, groups_fn(w, lens))
+    del inp, res
+    torch.cuda.empty_cache()
+
+
+def test_attn_full_c1():
+    _full("c1", lambda w, lens: all_groups(w))
+
+
+def test_attn_full_c2():
+    _full("c2", lambda w, lens: all_groups(w))
+
+
+def test_attn_full_c3():
+    _full("c3", lambda w, lens: [(0, 0), (31, 5), (63, 7)])
+
+
+def test_attn_full_c4():
+    def groups(w, lens):
+        empty_b = int(np.where((lens == 0).any(axis=0))[0][-1])
+        return [(0, 0), (11, 3), (12, 7), (empty_b, 2)]
+    _full("c4", groups)
