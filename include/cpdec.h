@@ -26,8 +26,7 @@
  *     F16/BF16 round to nearest even.
  *   - Natural logarithms throughout (lse values are ln of sums of e^score).
  *   - Reentrant and thread-safe; two calls that share a workspace must not
- *     overlap in time on the device (they would race on it).  The only
- *     mutable library state is a process-wide counter that tags each call.
+ *     overlap in time on the device (they would race on it).
  */
 #ifndef CPDEC_H
 #define CPDEC_H
@@ -88,6 +87,16 @@ typedef struct cpdec_attn_desc {
 size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
 
 /*
+ * The launch plan cpdec_attn_partial uses for `d`: the split-KV chunk length
+ * in tokens, the number of chunks per (shard, sequence, kv head) and the
+ * waves per workgroup.  Any output pointer may be NULL.  Errors: the same
+ * descriptor checks as cpdec_attn_partial (INVALID_ARG, UNSUPPORTED,
+ * ALIGNMENT); outputs are untouched on error.
+ */
+cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens,
+                             int32_t* num_chunks, int32_t* waves);
+
+/*
  * Per-shard decode attention (page section "Introduction").
  *
  * For every shard r, sequence b and query head hq, with L = lens[r*B + b] and
@@ -111,11 +120,11 @@ size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
  *   lse_part     device, float [R][B][Hq]
  *   workspace    device, at least cpdec_attn_workspace_bytes(d) bytes,
  *                256-byte aligned; may be NULL when that size is 0.  Scratch
- *                for the split-KV chunk partials and one arrival slot per
- *                (shard, sequence, kv head, head block).  Its contents on entry
- *                do not matter (no clearing is needed, also when one buffer
- *                serves descriptors of different shapes); a call that
- *                completes leaves every arrival slot at 0.
+ *                for the split-KV chunk partials; its contents on entry do not
+ *                matter (no clearing is needed, also when one buffer serves
+ *                descriptors of different shapes).  When that size is non-zero
+ *                the call enqueues two kernels (attention, then the merge of
+ *                each shard's chunk partials), otherwise one.
  *   stream       hipStream_t
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP (see above).
  */

@@ -14,8 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lib", "AttnDesc", "CpdecError", "attn_partial", "lse_merge", "attn_workspace_bytes",
-           "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS"]
+__all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "attn_partial", "lse_merge",
+           "attn_workspace_bytes", "attn_plan", "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpdec.so")
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.cpdec_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
         L.cpdec_attn_workspace_bytes.restype = sz
+        pi = ctypes.POINTER(ctypes.c_int32)
+        L.cpdec_attn_plan.argtypes = [ctypes.POINTER(AttnDesc), pi, pi, pi]
+        L.cpdec_attn_plan.restype = ctypes.c_int
         L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
         L.cpdec_attn_partial.restype = ctypes.c_int
@@ -87,13 +90,6 @@ def dtype_code(dt) -> int:
 DTYPE_CODES = {"fp32": F32, "fp16": F16, "bf16": BF16}
 
 
-def _stream(t, stream):
-    torch = _torch()
-    if stream is not None:
-        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
-
-
 def make_attn_desc(q, k_shards, *, kv_capacity=None, sm_scale=0.0, opart_dtype=None,
                    chunk_tokens=0) -> AttnDesc:
     """Descriptor from q [B, Hq, D] and K shards [B, Hkv, cap, D] (any strides
@@ -119,6 +115,15 @@ def make_attn_desc(q, k_shards, *, kv_capacity=None, sm_scale=0.0, opart_dtype=N
     return d
 
 
+def attn_plan(desc: AttnDesc) -> dict:
+    """The library's launch plan for a descriptor: chunk tokens, chunks, waves."""
+    c, n, wv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = lib().cpdec_attn_plan(ctypes.byref(desc), ctypes.byref(c), ctypes.byref(n), ctypes.byref(wv))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_attn_plan")
+    return dict(chunk_tokens=c.value, num_chunks=n.value, waves=wv.value)
+
+
 def attn_workspace_bytes(desc: AttnDesc) -> int:
     return int(lib().cpdec_attn_workspace_bytes(ctypes.byref(desc)))
 
@@ -138,64 +143,110 @@ def _workspace(device, nbytes):
     return ws
 
 
+class AttnCall:
+    """A cpdec_attn_partial call with its arguments marshalled once.
+
+    Calling it enqueues the kernel on the current stream (or ``stream``)."""
+
+    def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
+                 kv_capacity=None, workspace=None, chunk_tokens=0):
+        torch = _torch()
+        if len(k_shards) != len(v_shards):
+            raise ValueError("k_shards and v_shards differ in length")
+        for v, k in zip(v_shards, k_shards):
+            if v.shape != k.shape or v.stride() != k.stride():
+                raise ValueError("V shards must match K shards in shape and strides")
+        if not (q.is_contiguous() and o_part.is_contiguous() and lse_part.is_contiguous()
+                and lens.is_contiguous()):
+            raise ValueError("q, o_part, lse_part and lens must be contiguous")
+        if lens.dtype != torch.int32 or lse_part.dtype != torch.float32:
+            raise TypeError("lens must be int32 and lse_part float32")
+        desc = make_attn_desc(q, k_shards, kv_capacity=kv_capacity, sm_scale=sm_scale,
+                              opart_dtype=o_part.dtype, chunk_tokens=chunk_tokens)
+        R = len(k_shards)
+        if tuple(o_part.shape) != (R, desc.batch, desc.num_q_heads, desc.head_dim):
+            raise ValueError("o_part must be [R, B, Hq, D]")
+        if (tuple(lse_part.shape) != (R, desc.batch, desc.num_q_heads)
+                or tuple(lens.shape) != (R, desc.batch)):
+            raise ValueError("lse_part must be [R, B, Hq] and lens [R, B]")
+        self.workspace_bytes = attn_workspace_bytes(desc)
+        self.plan = attn_plan(desc)
+        if workspace is None and self.workspace_bytes > 0:
+            workspace = _workspace(q.device, self.workspace_bytes)
+        self._keep = (q, list(k_shards), list(v_shards), lens, o_part, lse_part, workspace)
+        self.desc = desc
+        self._device = q.device
+        ks = (ctypes.c_void_p * R)(*[k.data_ptr() for k in k_shards])
+        vs = (ctypes.c_void_p * R)(*[v.data_ptr() for v in v_shards])
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._args = [ctypes.byref(desc), q.data_ptr(), ks, vs, lens.data_ptr(), o_part.data_ptr(),
+                      lse_part.data_ptr(), ws_ptr, ws_bytes]
+        self._arrays = (ks, vs)
+
+    def __call__(self, stream=None):
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream(self._device).cuda_stream
+        rc = lib().cpdec_attn_partial(*self._args, s)
+        if rc != 0:
+            raise CpdecError(rc, "cpdec_attn_partial")
+
+
+class MergeCall:
+    """A cpdec_lse_merge call with its arguments marshalled once:
+    o_part [R, ..., D] and lse_part [R, ...] into out [..., D], lse_out [...]."""
+
+    def __init__(self, o_part, lse_part, out, lse_out=None):
+        R = o_part.shape[0]
+        D = o_part.shape[-1]
+        rows = o_part.numel() // (R * D)
+        if not (o_part.is_contiguous() and lse_part.is_contiguous() and out.is_contiguous()):
+            raise ValueError("o_part, lse_part and out must be contiguous")
+        if lse_part.numel() != R * rows or out.numel() != rows * D:
+            raise ValueError("shape mismatch between o_part, lse_part and out")
+        if lse_out is not None and (lse_out.numel() != rows or not lse_out.is_contiguous()):
+            raise ValueError("lse_out must hold one value per row")
+        self._keep = (o_part, lse_part, out, lse_out)
+        self._device = o_part.device
+        self.rows, self.R, self.D = rows, R, D
+        self._args = [o_part.data_ptr(), lse_part.data_ptr(), R, rows, D, dtype_code(o_part.dtype),
+                      dtype_code(out.dtype), out.data_ptr(),
+                      lse_out.data_ptr() if lse_out is not None else None]
+
+    def __call__(self, stream=None):
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream(self._device).cuda_stream
+        rc = lib().cpdec_lse_merge(*self._args, s)
+        if rc != 0:
+            raise CpdecError(rc, "cpdec_lse_merge")
+
+
 def attn_partial(q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
                  kv_capacity=None, workspace=None, chunk_tokens=0, stream=None):
     """Per-shard decode attention into o_part [R,B,Hq,D] and lse_part [R,B,Hq].
 
     lens: int32 device tensor [R, B]."""
-    torch = _torch()
-    if len(k_shards) != len(v_shards):
-        raise ValueError("k_shards and v_shards differ in length")
-    for v, k in zip(v_shards, k_shards):
-        if v.shape != k.shape or v.stride() != k.stride():
-            raise ValueError("V shards must match K shards in shape and strides")
-    if not (q.is_contiguous() and o_part.is_contiguous() and lse_part.is_contiguous()
-            and lens.is_contiguous()):
-        raise ValueError("q, o_part, lse_part and lens must be contiguous")
-    if lens.dtype != torch.int32 or lse_part.dtype != torch.float32:
-        raise TypeError("lens must be int32 and lse_part float32")
-    desc = make_attn_desc(q, k_shards, kv_capacity=kv_capacity, sm_scale=sm_scale,
-                          opart_dtype=o_part.dtype, chunk_tokens=chunk_tokens)
-    R = len(k_shards)
-    if tuple(o_part.shape) != (R, desc.batch, desc.num_q_heads, desc.head_dim):
-        raise ValueError("o_part must be [R, B, Hq, D]")
-    if tuple(lse_part.shape) != (R, desc.batch, desc.num_q_heads) or tuple(lens.shape) != (R, desc.batch):
-        raise ValueError("lse_part must be [R, B, Hq] and lens [R, B]")
-    need = attn_workspace_bytes(desc)
-    if workspace is None and need > 0:
-        workspace = _workspace(q.device, need)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    ks = (ctypes.c_void_p * R)(*[k.data_ptr() for k in k_shards])
-    vs = (ctypes.c_void_p * R)(*[v.data_ptr() for v in v_shards])
-    rc = lib().cpdec_attn_partial(ctypes.byref(desc), q.data_ptr(), ks, vs, lens.data_ptr(),
-                                  o_part.data_ptr(), lse_part.data_ptr(), ws_ptr, ws_bytes,
-                                  _stream(q, stream))
-    if rc != 0:
-        raise CpdecError(rc, "cpdec_attn_partial")
+    AttnCall(q, k_shards, v_shards, lens, o_part, lse_part, sm_scale=sm_scale,
+             kv_capacity=kv_capacity, workspace=workspace, chunk_tokens=chunk_tokens)(
+                 _stream_handle(stream))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, *, stream=None):
     """Merge o_part [R, ..., D] with lse_part [R, ...] into out [..., D] and lse_out [...]."""
-    R = o_part.shape[0]
-    D = o_part.shape[-1]
-    rows = o_part.numel() // (R * D)
-    if not (o_part.is_contiguous() and lse_part.is_contiguous() and out.is_contiguous()):
-        raise ValueError("o_part, lse_part and out must be contiguous")
-    if lse_part.numel() != R * rows or out.numel() != rows * D:
-        raise ValueError("shape mismatch between o_part, lse_part and out")
-    if lse_out is not None and (lse_out.numel() != rows or not lse_out.is_contiguous()):
-        raise ValueError("lse_out must hold one value per row")
-    rc = lib().cpdec_lse_merge(o_part.data_ptr(), lse_part.data_ptr(), R, rows, D,
-                               dtype_code(o_part.dtype), dtype_code(out.dtype), out.data_ptr(),
-                               lse_out.data_ptr() if lse_out is not None else None,
-                               _stream(o_part, stream))
-    if rc != 0:
-        raise CpdecError(rc, "cpdec_lse_merge")
+    MergeCall(o_part, lse_part, out, lse_out)(_stream_handle(stream))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def workspace_clear(ws, *, stream=None):
-    rc = lib().cpdec_workspace_clear(ws.data_ptr(), ws.numel() * ws.element_size(),
-                                     _stream(ws, stream))
+    torch = _torch()
+    s = _stream_handle(stream)
+    if s is None:
+        s = torch.cuda.current_stream(ws.device).cuda_stream
+    rc = lib().cpdec_workspace_clear(ws.data_ptr(), ws.numel() * ws.element_size(), s)
     if rc != 0:
         raise CpdecError(rc, "cpdec_workspace_clear")

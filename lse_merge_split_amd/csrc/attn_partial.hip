@@ -11,11 +11,15 @@
 //           (unit, chunk), chunks at or past L exit at once.
 //   A workgroup has NW waves; wave w takes the 32-token tiles w, w+NW, ... of
 //   its chunk and keeps an online-softmax state (running max m, exp-sum l,
-//   un-normalised accumulator) per query head.  The waves' states are merged
-//   through LDS, and the chunks of a unit are merged by the last workgroup to
-//   finish (a tagged arrival slot in the workspace) -- both with the same LSE
+//   un-normalised accumulator) per query head, loading tile i+1 while it
+//   computes tile i.  The waves' states are merged through LDS.  A unit whose
+//   tokens fit one chunk is written straight to o_part/lse_part; otherwise each
+//   chunk writes a normalised partial to the workspace and a second, small
+//   kernel merges the chunks of every unit -- both merges use the same LSE
 //   weighting as the cross-shard merge, which the page's merge formula makes
-//   exact.
+//   exact.  No workgroup waits on another inside a kernel: on gfx950 a
+//   device-scope release/acquire pair writes back and invalidates the L2 of
+//   the XCD, which costs more than a second launch.
 //
 // Per 32-token tile, with G <= 16 query heads of one kv head as MFMA columns:
 //   S^T[t][g] = K[t][:] . Q[g][:]       4 (D/32) MFMA 16x16x32 per 16 tokens;
@@ -88,18 +92,9 @@ __device__ __forceinline__ void store4(void* base, int64_t idx, f32x4 x, int odt
 template <int D, int NW>
 struct Smem {
   static constexpr int NB = (D / 8 + 15) / 16;
-  union {
-    struct {
-      f32x4 acc[NW > 1 ? NW - 1 : 1][NB * 8][64];
-      float m[NW][16];
-      float l[NW][16];
-    } waves;
-    struct {
-      float w[kMaxChunks][16];
-      float lse[16];
-    } chunks;
-  };
-  int last;
+  f32x4 acc[NW > 1 ? NW - 1 : 1][NB * 8][64];
+  float m[NW][16];
+  float l[NW][16];
 };
 
 template <typename T, int D, int NW>
@@ -160,9 +155,9 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[nb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = t_begin + wave * kTileTokens; t0 < t_end; t0 += NW * kTileTokens) {
-    // ---- loads: K rows into the A operand, V rows for the transpose ----
-    u32x4 kr[2][KS];
+  // K rows go straight into the A operand (lane = token row l16, 8 contiguous
+  // d per k-step); V rows are loaded for the in-register transpose.
+  auto load_tile = [&](int t0, u32x4 (&kr)[2][KS], u32x4 (&vr)[NB][8]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int t = min(t0 + 16 * blk + l16, L - 1);
@@ -170,7 +165,6 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 #pragma unroll
       for (int s = 0; s < KS; ++s) kr[blk][s] = ld16(kp + 32 * s);
     }
-    u32x4 vr[NB][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = min(t0 + tile_token(q4, j), L - 1);
@@ -181,6 +175,16 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         vr[nb][j] = (ch < NCH) ? ld16(vp + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+
+  u32x4 kr[2][KS], vr[NB][8];
+  int t0 = t_begin + wave * kTileTokens;
+  if (t0 < t_end) load_tile(t0, kr, vr);
+  for (; t0 < t_end; t0 += NW * kTileTokens) {
+    // prefetch the wave's next tile while this one is computed
+    u32x4 krn[2][KS], vrn[NB][8];
+    const int tn = t0 + NW * kTileTokens;
+    if (tn < t_end) load_tile(tn, krn, vrn);
 
     // ---- scores S^T (16 tokens x 16 heads per block), base-2 scaled, masked ----
     float x[2][4];
@@ -234,6 +238,14 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         acc[nb][n] = mfma16x16x32<T>(va, plo, a);
       }
     }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kr[blk][s] = krn[blk][s];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vr[nb][j] = vrn[nb][j];
   }
 
   lsum += __shfl_xor(lsum, 16);
@@ -245,10 +257,10 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) sm.waves.acc[wave - 1][nb * 8 + n][lane] = acc[nb][n];
+        for (int n = 0; n < 8; ++n) sm.acc[wave - 1][nb * 8 + n][lane] = acc[nb][n];
       if (q4 == 0) {
-        sm.waves.m[wave][l16] = m;
-        sm.waves.l[wave][l16] = lsum;
+        sm.m[wave][l16] = m;
+        sm.l[wave][l16] = lsum;
       }
     }
     __syncthreads();
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
       float M = m;
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
-        mw[w] = sm.waves.m[w][l16];
+        mw[w] = sm.m[w][l16];
         M = fmaxf(M, mw[w]);
       }
       const float a0 = exp2f(m - M);  // M finite: wave 0 saw the chunk's first tile
@@ -269,11 +281,11 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
         const float aw = exp2f(mw[w] - M);  // 0 for a wave that saw no tile
-        lsum += aw * sm.waves.l[w][l16];
+        lsum += aw * sm.l[w][l16];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int n = 0; n < 8; ++n) acc[nb][n] += aw * sm.waves.acc[w - 1][nb * 8 + n][lane];
+          for (int n = 0; n < 8; ++n) acc[nb][n] += aw * sm.acc[w - 1][nb * 8 + n][lane];
       }
       m = M;
     }
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     return;
   }
 
-  // ---- several live chunks: publish this chunk's partial, last one merges ----
+  // ---- several live chunks: this chunk's normalised partial to the workspace ----
   const int64_t slot = (int64_t)unit * p.nchunks + c;
   if (wave == 0 && l16 < ng) {
 #pragma unroll
@@ -318,31 +330,27 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     }
     if (q4 == 0) p.ws_lse[slot * p.Gb + l16] = lse_nat;
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // Arrival slot = (tag << 16) | count.  A slot holding any other tag (left
-    // over from another shape, a stale buffer, garbage) restarts at count 1,
-    // so the workspace needs no clearing; the last arrival resets it to 0.
-    unsigned long long* slot = p.ws_cnt + unit;
-    const unsigned long long tag = p.tag << 16;
-    unsigned long long old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long nv;
-    for (;;) {
-      nv = ((old & ~0xffffull) == tag) ? old + 1ull : (tag | 1ull);
-      const unsigned long long prev = atomicCAS(slot, old, nv);
-      if (prev == old) break;
-      old = prev;
-    }
-    sm.last = (int)((nv & 0xffffull) == (unsigned long long)nlive);
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
+}
 
-  // Last arrival: merge the nlive chunk partials of this unit (same weighting
-  // as the cross-shard merge) into o_part / lse_part.
+// Merge the chunk partials of every unit that has more than one live chunk
+// (one workgroup per unit), with the LSE weighting of the cross-shard merge.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  __shared__ float w[kMaxChunks][16];
+  const int unit = blockIdx.x;
+  int u = unit;
+  const int gb = u % p.gblocks; u /= p.gblocks;
+  const int h = u % p.Hkv; u /= p.Hkv;
+  const int b = u % p.B;
+  const int r = u / p.B;
+  const int L = p.lens[r * p.B + b];
+  const int nlive = (L + p.chunk - 1) / p.chunk;
+  if (nlive < 2) return;  // written directly by the attention kernel
+  const int g0 = gb * kGroupRows;
+  const int ng = min(kGroupRows, p.G - g0);
+  const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
   const int64_t slot0 = (int64_t)unit * p.nchunks;
+
   if (threadIdx.x < ng) {
     const int g = threadIdx.x;
     float M = neg_inf();
@@ -350,24 +358,22 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     float S = 0.f;
     for (int cc = 0; cc < nlive; ++cc) {
       const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
-      sm.chunks.w[cc][g] = e;
+      w[cc][g] = e;
       S += e;
     }
     const float invS = 1.0f / S;
-    for (int cc = 0; cc < nlive; ++cc) sm.chunks.w[cc][g] *= invS;
+    for (int cc = 0; cc < nlive; ++cc) w[cc][g] *= invS;
     p.lse_part[orow0 + g] = M + logf(S);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < ng * (D / 4); e += NW * 64) {
+  for (int e = threadIdx.x; e < ng * (D / 4); e += 256) {
     const int g = e / (D / 4);
     const int d = 4 * (e % (D / 4));
     f32x4 y = {0.f, 0.f, 0.f, 0.f};
     for (int cc = 0; cc < nlive; ++cc)
-      y += sm.chunks.w[cc][g] *
-           *reinterpret_cast<const f32x4*>(p.ws_o + ((slot0 + cc) * p.Gb + g) * D + d);
+      y += w[cc][g] * *reinterpret_cast<const f32x4*>(p.ws_o + ((slot0 + cc) * p.Gb + g) * D + d);
     store4(p.o_part, (orow0 + g) * D + d, y, p.odt);
   }
-  if (threadIdx.x == 0) p.ws_cnt[unit] = 0ull;  // slot free again (graph replays reuse the tag)
 }
 
 template <typename T, int D, int NW>
@@ -375,6 +381,9 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, hipStream_t s) {
   const int64_t blocks = units * p.nchunks;
   hipLaunchKernelGGL((attn_partial_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, s,
                      p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nchunks < 2) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,6 +1,5 @@
 // cpdec_api.hip -- the C ABI of libcpdec (include/cpdec.h): argument checks,
 // launch planning and kernel dispatch.  Every check runs before any HIP call.
-#include <atomic>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -99,8 +98,8 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
 
   if (p.nchunks > 1) {
     const size_t slots = (size_t)p.units * p.nchunks * p.Gb;
-    p.off_lse = round256((size_t)p.units * sizeof(unsigned long long));
-    p.off_o = p.off_lse + round256(slots * sizeof(float));
+    p.off_lse = 0;
+    p.off_o = round256(slots * sizeof(float));
     p.ws_bytes = p.off_o + slots * (size_t)D * sizeof(float);
   }
   *pl = p;
@@ -108,17 +107,6 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
 }
 
 size_t dtype_size(int dt) { return dt == CPDEC_F32 ? 4 : 2; }
-
-// Tags that mark which call an arrival slot belongs to: 48-bit, never 0, a
-// new one per call (a process-wide counter; the only mutable library state).
-unsigned long long next_call_tag() {
-  static std::atomic<unsigned long long> calls{0};
-  unsigned long long t;
-  do {
-    t = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
-  } while (t == 0);
-  return t;
-}
 
 }  // namespace
 
@@ -128,6 +116,17 @@ size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d) {
   AttnPlan pl;
   if (plan_attn(d, &pl) != CPDEC_OK) return 0;
   return pl.ws_bytes;
+}
+
+cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens, int32_t* num_chunks,
+                             int32_t* waves) {
+  AttnPlan pl;
+  const cpdec_status st = plan_attn(d, &pl);
+  if (st != CPDEC_OK) return st;
+  if (chunk_tokens) *chunk_tokens = pl.chunk;
+  if (num_chunks) *num_chunks = pl.nchunks;
+  if (waves) *waves = pl.waves;
+  return CPDEC_OK;
 }
 
 cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
@@ -165,7 +164,6 @@ cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
   p.lse_part = lse_part;
   if (pl.ws_bytes > 0) {
     char* ws = static_cast<char*>(workspace);
-    p.ws_cnt = reinterpret_cast<unsigned long long*>(ws);
     p.ws_lse = reinterpret_cast<float*>(ws + pl.off_lse);
     p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   }
@@ -184,7 +182,6 @@ cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
   p.odt = d->opart_dtype;
   const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
-  p.tag = next_call_tag();
 
   hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units,
                                      static_cast<hipStream_t>(stream));

@@ -23,14 +23,13 @@ struct AttnParams {
   float* lse_part;
   float* ws_o;        // [units][nchunks][Gb][D] chunk partials (normalised)
   float* ws_lse;      // [units][nchunks][Gb]    chunk lse (natural log)
-  unsigned long long* ws_cnt;  // [units] arrival slots: (call tag << 16) | count
   int64_t sb, sh, st; // K/V element strides: batch, head, token
   int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, odt;
   float scale_log2;   // sm_scale * log2(e)
-  unsigned long long tag;  // per-call tag, 1 .. 2^48-1
 };
 
-// Launch the partial-attention kernel over units x nchunks workgroups.
+// Launch the partial-attention kernel over units x nchunks workgroups, then
+// (when a unit can span several chunks) the chunk-combine kernel over units.
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
                                int64_t units, hipStream_t s);
 

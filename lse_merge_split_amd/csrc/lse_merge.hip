@@ -10,10 +10,11 @@
 //   * One row group of GS lanes per output row; each lane owns 16-byte
 //     vectors of the row (D=512 bf16: one wave per row, one 16-byte load per
 //     lane per shard; D=128 fp32: two rows per wave).
-//   * Weights are formed in FP64 (one exp per shard) so the merged lse keeps
-//     ~1e-7 relative accuracy even when it cancels towards 0; the o sum is FP32
-//     in shard order and the division by the weight sum is applied once at the
-//     end.
+//   * Weights are formed in FP64 so the merged lse keeps ~1e-7 relative
+//     accuracy even when it cancels towards 0.  Lane j of a row group computes
+//     the one exp of shard j and the weights reach the other lanes by shuffles;
+//     the weight sum (FP64) and the o sum (FP32) run in shard order, and the
+//     division by the weight sum is applied once at the end.
 //   * Shards with lse = -inf are skipped before their row is loaded: their
 //     bytes are never read and any garbage/NaN in them cannot leak.
 //   * Loads of a batch of 8 shards are issued back to back before any use so
@@ -79,28 +80,35 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   constexpr int GS = NV < 64 ? NV : 64;    // lanes per row
   constexpr int RPW = 64 / GS;             // rows per wave
   constexpr int VPL = NV / GS;             // vectors per lane
-  static_assert(NV % GS == 0 && 64 % GS == 0, "row split");
+  static_assert(NV % GS == 0 && 64 % GS == 0 && GS >= kBatch, "row split");
 
   const int lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW + lane / GS;
+  const int64_t row_raw = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW + lane / GS;
+  const bool valid = row_raw < rows;
+  const int64_t row = valid ? row_raw : rows - 1;  // idle lanes shadow a real row
   const int li = lane % GS;
-  if (row >= rows) return;
-
+  const int base = lane - li;                      // first lane of this row group
   const float* lrow = lse + row;
+
+  // Row max over shards: lane li reads shards li, li+GS, ..., then the group reduces.
   float M = neg_inf();
-  for (int r = 0; r < R; ++r) M = fmaxf(M, lrow[(int64_t)r * rows]);
+  for (int r = li; r < R; r += GS) M = fmaxf(M, lrow[(int64_t)r * rows]);
+#pragma unroll
+  for (int off = GS / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, GS));
 
   Tout* orow = out + row * D;
   if (M == neg_inf()) {  // every shard empty: out = 0, lse = -inf
-    float z[VEC] = {};
+    if (valid) {
+      float z[VEC] = {};
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, z);
-    if (lse_out != nullptr && li == 0) lse_out[row] = neg_inf();
+      for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, z);
+      if (lse_out != nullptr && li == 0) lse_out[row] = neg_inf();
+    }
     return;
   }
 
   const double Md = (double)M;
-  double S = 0.0;
+  double S = 0.0;  // weight sum, accumulated in shard order
   float acc[VPL][VEC];
 #pragma unroll
   for (int v = 0; v < VPL; ++v)
@@ -108,35 +116,42 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
     for (int e = 0; e < VEC; ++e) acc[v][e] = 0.f;
 
   const Tin* obase = o + row * D + li * VEC;
-  for (int rb = 0; rb < R; rb += kBatch) {
-    float lb[kBatch];
-    u32x4 raw[kBatch][VPL];
+  for (int rb = 0; rb < R; rb += GS) {
+    // one FP64 exp per lane: lane li owns shard rb + li of this block
+    const int rl = rb + li;
+    const float lme = (rl < R) ? lrow[(int64_t)rl * rows] : neg_inf();
+    const double eme = (lme != neg_inf()) ? exp((double)lme - Md) : 0.0;
+    const int nb = min(GS, R - rb);
+    for (int j0 = 0; j0 < nb; j0 += kBatch) {
+      double e[kBatch];
+      u32x4 raw[kBatch][VPL];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int r = rb + j;
-      lb[j] = (r < R) ? lrow[(int64_t)r * rows] : neg_inf();
-      if (lb[j] != neg_inf()) {
-        const Tin* src = obase + (int64_t)r * rows * D;
+      for (int j = 0; j < kBatch; ++j) {
+        const int src = base + ((j0 + j) < nb ? (j0 + j) : 0);
+        e[j] = (j0 + j < nb) ? __shfl(eme, src) : 0.0;
+        if (e[j] != 0.0) {  // empty shards (and weights below FP64 range) are never read
+          const Tin* sp = obase + (int64_t)(rb + j0 + j) * rows * D;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(src + v * GS * VEC);
+          for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(sp + v * GS * VEC);
+        }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (lb[j] == neg_inf()) continue;  // empty shard: skipped, never read
-      const double e = exp((double)lb[j] - Md);
-      S += e;
-      const float w = (float)e;
+      for (int j = 0; j < kBatch; ++j) {
+        if (e[j] == 0.0) continue;
+        S += e[j];
+        const float wj = (float)e[j];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        float x[VEC];
-        InVec<Tin>::cvt(raw[j][v], x);
+        for (int v = 0; v < VPL; ++v) {
+          float x[VEC];
+          InVec<Tin>::cvt(raw[j][v], x);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(w, x[k], acc[v][k]);
+          for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(wj, x[k], acc[v][k]);
+        }
       }
     }
   }
 
+  if (!valid) return;
   const float inv = (float)(1.0 / S);
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {

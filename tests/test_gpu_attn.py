@@ -104,8 +104,7 @@ def test_attn_padding_is_never_read():
 
 
 def test_attn_workspace_reuse_and_determinism():
-    """Two calls on one workspace give identical bits (the arrival counters
-    are left at zero)."""
+    """Two calls on one workspace give identical bits."""
     w = SMALL["c3_small"]
     _say("attn workspace reuse")
     inp = sg.attn_inputs(w)
@@ -113,8 +112,6 @@ def test_attn_workspace_reuse_and_determinism():
     ws = torch.zeros(cp.attn_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     a = run_path(inp, chunk_tokens=128, workspace=ws)
     b = run_path(inp, chunk_tokens=128, workspace=ws)
-    units = w.R * w.B * w.Hkv            # one 8-byte arrival slot per unit
-    assert torch.count_nonzero(ws[:8 * units]).item() == 0
     for key in a:
         assert torch.equal(a[key], b[key]), key
 
