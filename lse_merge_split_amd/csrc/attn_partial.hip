@@ -8,7 +8,8 @@
 // Work decomposition
 //   unit  = (shard r, sequence b, kv head h, block of <= 16 query heads of h)
 //   chunk = `chunk` consecutive tokens of a unit; one workgroup per
-//           (unit, chunk), chunks at or past L exit at once.
+//           (unit, chunk) in chunk-major order, chunks at or past L exit at
+//           once.
 //   A workgroup has NW waves; wave w takes the 32-token tiles w, w+NW, ... of
 //   its chunk and keeps an online-softmax state (running max m, exp-sum l,
 //   un-normalised accumulator) per query head, loading tile i+1 while it
@@ -109,8 +110,11 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  const int c = blockIdx.x % p.nchunks;
-  const int unit = blockIdx.x / p.nchunks;
+  // Chunk-major order: workgroups are dealt to the 8 XCDs round-robin by
+  // block index, so block % 8 must not correlate with the chunk index (the
+  // later chunks of ragged shards are mostly empty); here it follows the unit.
+  const int c = blockIdx.x / p.units;
+  const int unit = blockIdx.x % p.units;
   int u = unit;
   const int gb = u % p.gblocks; u /= p.gblocks;
   const int h = u % p.Hkv; u /= p.Hkv;

@@ -38,7 +38,6 @@ const Overrides& overrides() {
 }
 
 constexpr int kDefaultWaves = 4;
-constexpr int kMaxChunkTokens = 2048;   // longest chunk the planner picks
 constexpr int64_t kTargetBlocks = 2048; // workgroups the planner aims for
 
 struct AttnPlan {
@@ -82,10 +81,12 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
 
   int chunk = d->chunk_tokens ? d->chunk_tokens : overrides().chunk;
   if (chunk == 0) {
-    chunk = kMaxChunkTokens;
-    while (chunk > span && p.units * ceil_div(cap, chunk) < kTargetBlocks) chunk /= 2;
-    if (chunk < span) chunk = span;
-    if (chunk > cap) chunk = (int)ceil_div(cap, kTileTokens) * kTileTokens;
+    // Split a shard into chunks only as far as needed to give the GPU
+    // kTargetBlocks workgroups: every chunk costs a partial write and a merge.
+    int64_t want = ceil_div(kTargetBlocks, p.units);
+    const int64_t most = ceil_div(cap, span);      // chunks of one pass of all waves
+    if (want > most) want = most;
+    chunk = (int)(ceil_div(ceil_div(cap, want), span) * span);
   }
   if (ceil_div(cap, chunk) > kMaxChunks)
     chunk = (int)ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
@@ -93,7 +94,8 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   p.nchunks = (int)ceil_div(cap, chunk);
 
   const int64_t blocks = p.units * p.nchunks;
-  if (blocks > INT32_MAX || (int64_t)d->num_shards * d->batch * d->num_q_heads > INT32_MAX)
+  if (blocks > INT32_MAX || p.units > INT32_MAX ||
+      (int64_t)d->num_shards * d->batch * d->num_q_heads > INT32_MAX)
     return CPDEC_ERR_INVALID_ARG;
 
   if (p.nchunks > 1) {
@@ -179,6 +181,7 @@ cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
   p.R = d->num_shards;
   p.chunk = pl.chunk;
   p.nchunks = pl.nchunks;
+  p.units = (int32_t)pl.units;
   p.odt = d->opart_dtype;
   const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);

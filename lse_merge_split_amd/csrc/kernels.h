@@ -24,7 +24,7 @@ struct AttnParams {
   float* ws_o;        // [units][nchunks][Gb][D] chunk partials (normalised)
   float* ws_lse;      // [units][nchunks][Gb]    chunk lse (natural log)
   int64_t sb, sh, st; // K/V element strides: batch, head, token
-  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, odt;
+  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt;
   float scale_log2;   // sm_scale * log2(e)
 };
 

@@ -18,7 +18,9 @@
 //   * Shards with lse = -inf are skipped before their row is loaded: their
 //     bytes are never read and any garbage/NaN in them cannot leak.
 //   * Loads of a batch of 8 shards are issued back to back before any use so
-//     8 x 16 bytes per lane are in flight.
+//     8 x 16 bytes per lane are in flight.  For R <= 8 a persistent,
+//     software-pipelined form overlaps the next row's lse fetch with this
+//     row's partial loads; larger R uses one wave per row and batches of 8.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -163,6 +165,124 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   if (lse_out != nullptr && li == 0) lse_out[row] = (float)(Md + log(S));
 }
 
+// Pipelined form for R <= kBatch (every shard's 16-byte vectors in flight
+// together): persistent waves walk rows with a stride; while the partial rows
+// of row k are loading, the lse values of row k+1 are already requested, so a
+// row costs one memory round trip.  Lane li of a row group owns shard li's lse
+// and its FP64 exp; shuffles hand the values to the other lanes.
+template <typename Tin, typename Tout, int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_pipelined_kernel(
+    const Tin* __restrict__ o, const float* __restrict__ lse, int R, int64_t rows,
+    Tout* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int VEC = InVec<Tin>::N;
+  constexpr int NV = D / VEC;
+  constexpr int GS = NV < 64 ? NV : 64;
+  constexpr int RPW = 64 / GS;
+  constexpr int VPL = NV / GS;
+  static_assert(GS >= kBatch, "a row group must hold one lane per shard");
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % GS;
+  const int base = lane - li;
+  const int64_t step = (int64_t)gridDim.x * kMergeWaves * RPW;
+  int64_t wrow = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW;
+
+  float l_next = neg_inf();
+  {
+    const int64_t row = wrow + lane / GS;
+    if (row < rows && li < R) l_next = lse[(int64_t)li * rows + row];
+  }
+  for (; wrow < rows; wrow += step) {
+    const int64_t row = wrow + lane / GS;
+    const bool valid = row < rows;
+    const float l_own = l_next;
+
+    // every shard's lse in every lane of the group; issue the live rows' loads
+    float lj[kBatch];
+    u32x4 raw[kBatch][VPL];
+    const Tin* obase = o + (valid ? row : 0) * D + li * VEC;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      lj[j] = __shfl(l_own, base + j);
+      if (j >= R) lj[j] = neg_inf();
+      if (valid && lj[j] != neg_inf()) {
+        const Tin* sp = obase + (int64_t)j * rows * D;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(sp + v * GS * VEC);
+      }
+    }
+    // request the next row's lse while these loads are in flight
+    {
+      const int64_t nrow = row + step;
+      l_next = (nrow < rows && li < R) ? lse[(int64_t)li * rows + nrow] : neg_inf();
+    }
+
+    float M = lj[0];
+#pragma unroll
+    for (int j = 1; j < kBatch; ++j) M = fmaxf(M, lj[j]);
+    Tout* orow = out + (valid ? row : 0) * D;
+    if (M == neg_inf()) {  // every shard empty
+      if (valid) {
+        float z[VEC] = {};
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, z);
+        if (lse_out != nullptr && li == 0) lse_out[row] = neg_inf();
+      }
+      continue;
+    }
+    const double Md = (double)M;
+    const double e_own = (l_own != neg_inf() && li < R) ? exp((double)l_own - Md) : 0.0;
+    double S = 0.0;
+    float acc[VPL][VEC];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[v][k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const double ej = __shfl(e_own, base + j);
+      if (lj[j] == neg_inf() || ej == 0.0) continue;
+      S += ej;
+      const float wj = (float)ej;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        float x[VEC];
+        InVec<Tin>::cvt(raw[j][v], x);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(wj, x[k], acc[v][k]);
+      }
+    }
+    if (!valid) continue;
+    const float inv = (float)(1.0 / S);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      float y[VEC];
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) y[k] = acc[v][k] * inv;
+      store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, y);
+    }
+    if (lse_out != nullptr && li == 0) lse_out[row] = (float)(Md + log(S));
+  }
+}
+
+// Resident workgroups per CU x CUs for a kernel on the current device
+// (queried once per device and kernel; a benign race recomputes the same value).
+template <typename K>
+int64_t resident_blocks(K kernel, int threads) {
+  static int64_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 1024;
+    cache[dev] = (int64_t)cus * per_cu;
+  }
+  return cache[dev];
+}
+
 template <typename Tin, typename Tout, int D>
 hipError_t launch_typed(const void* o, const float* lse, int R, int64_t rows, void* out,
                         float* lse_out, hipStream_t s) {
@@ -172,6 +292,14 @@ hipError_t launch_typed(const void* o, const float* lse, int R, int64_t rows, vo
   constexpr int rows_per_block = kMergeWaves * (64 / GS);
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks == 0) return hipSuccess;
+  if (R <= kBatch) {
+    auto kern = lse_merge_pipelined_kernel<Tin, Tout, D>;
+    int64_t grid = resident_blocks(kern, kMergeWaves * 64);
+    if (grid > blocks) grid = blocks;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMergeWaves * 64), 0, s,
+                       static_cast<const Tin*>(o), lse, R, rows, static_cast<Tout*>(out), lse_out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D>), dim3((unsigned)blocks),
                      dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
                      static_cast<Tout*>(out), lse_out);
