@@ -66,7 +66,10 @@ typedef struct cpdec_attn_desc {
   int32_t head_dim;       /* D in {64, 128, 256}                             */
   int32_t num_shards;     /* R in [1, CPDEC_MAX_SHARDS]                      */
   int32_t kv_capacity;    /* tokens allocated per (shard, sequence, kv head);
-                             every lens entry must be <= kv_capacity        */
+                             every lens entry must be <= kv_capacity.
+                             kv_capacity * kv_stride_token * 2 must stay
+                             below 2^31 (32-bit offsets within one
+                             (shard, sequence, kv head); else UNSUPPORTED)  */
   int64_t kv_stride_batch; /* element strides of each K/V shard tensor;     */
   int64_t kv_stride_head;  /* the D elements of a token are contiguous.     */
   int64_t kv_stride_token; /* [B][Hkv][cap][D] contiguous is
@@ -153,7 +156,9 @@ cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
  *   lse_part   device, float [R][rows]; entries finite or -inf (NaN and +inf
  *              are outside the contract)
  *   num_shards R in [1, CPDEC_MAX_SHARDS]
- *   rows       >= 0 (0 enqueues nothing)
+ *   rows       >= 0 (0 enqueues nothing); rows * head_dim * sizeof(in) and
+ *              num_shards * rows * 4 must stay below 2^31 (32-bit offsets
+ *              within one shard; else UNSUPPORTED)
  *   head_dim   in {64, 128, 256, 512}
  *   in_dtype   CPDEC_F32, CPDEC_F16 or CPDEC_BF16
  *   out_dtype  CPDEC_F32, CPDEC_F16 or CPDEC_BF16

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
   __shared__ Smem<D, NW> sm;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
@@ -161,34 +161,39 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 
   // K rows go straight into the A operand (lane = token row l16, 8 contiguous
   // d per k-step); V rows are loaded for the in-register transpose.
+  // K/V of this unit through buffer resources ending at the chunk's last
+  // token: rows past it read as zeros without memory traffic, so the tail and
+  // the prefetch beyond the end need neither clamping nor a branch (a branch
+  // around loads makes the compiler drain every outstanding load at the join).
+  const uint32_t span = (uint32_t)(((int64_t)(t_end - 1) * st + D) * sizeof(T));
+  const rsrc_t krs = make_rsrc(kb, span);
+  const rsrc_t vrs = make_rsrc(vb, span);
+  const uint32_t rowb = (uint32_t)(st * sizeof(T));  // bytes per token row
   auto load_tile = [&](int t0, u32x4 (&kr)[2][KS], u32x4 (&vr)[NB][8]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int t = min(t0 + 16 * blk + l16, L - 1);
-      const T* kp = kb + t * st + 8 * q4;
+      const uint32_t off = (uint32_t)(t0 + 16 * blk + l16) * rowb + 16u * q4;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[blk][s] = ld16(kp + 32 * s);
+      for (int s = 0; s < KS; ++s) kr[blk][s] = buf16_stream(krs, off + 64u * s);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int t = min(t0 + tile_token(q4, j), L - 1);
-      const T* vp = vb + t * st;
+      const uint32_t off = (uint32_t)(t0 + tile_token(q4, j)) * rowb;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int ch = 16 * nb + l16;
-        vr[nb][j] = (ch < NCH) ? ld16(vp + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+        vr[nb][j] = buf16_stream(vrs, (ch < NCH) ? off + 16u * ch : kOutOfRange);
       }
     }
   };
 
   u32x4 kr[2][KS], vr[NB][8];
   int t0 = t_begin + wave * kTileTokens;
-  if (t0 < t_end) load_tile(t0, kr, vr);
+  load_tile(t0, kr, vr);
   for (; t0 < t_end; t0 += NW * kTileTokens) {
     // prefetch the wave's next tile while this one is computed
     u32x4 krn[2][KS], vrn[NB][8];
-    const int tn = t0 + NW * kTileTokens;
-    if (tn < t_end) load_tile(tn, krn, vrn);
+    load_tile(t0 + NW * kTileTokens, krn, vrn);
 
     // ---- scores S^T (16 tokens x 16 heads per block), base-2 scaled, masked ----
     float x[2][4];
@@ -211,6 +216,9 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);  // finite: the tile holds >= 1 live token
     const float alpha = exp2f(m - m_new);
+    // rescale the accumulators only when some head's running max grew
+    // (rare after the first tiles); the branch is wave-uniform and holds no loads
+    const bool grew = __any(m_new > m);
     m = m_new;
     float pr[8];
 #pragma unroll
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         u32x4 va;
 #pragma unroll
         for (int k = 0; k < 4; ++k) va[k] = perm_b32(vr[nb][2 * k + 1][w], vr[nb][2 * k][w], sel);
-        f32x4 a = acc[nb][n] * alpha;
+        f32x4 a = grew ? acc[nb][n] * alpha : acc[nb][n];
         a = mfma16x16x32<T>(va, phi, a);
         acc[nb][n] = mfma16x16x32<T>(va, plo, a);
       }
@@ -337,10 +345,15 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 }
 
 // Merge the chunk partials of every unit that has more than one live chunk
-// (one workgroup per unit), with the LSE weighting of the cross-shard merge.
+// (one 256-thread workgroup per unit), with the LSE weighting of the
+// cross-shard merge.  Per-head statistics use wave reductions over chunks;
+// the weighted sum splits the chunks over P thread groups when the unit has
+// fewer than 256 float4 outputs, and the groups are added in a fixed order
+// (results do not depend on timing).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   __shared__ float w[kMaxChunks][16];
+  __shared__ f32x4 part[256];
   const int unit = blockIdx.x;
   int u = unit;
   const int gb = u % p.gblocks; u /= p.gblocks;
@@ -354,29 +367,56 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const int ng = min(kGroupRows, p.G - g0);
   const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
   const int64_t slot0 = (int64_t)unit * p.nchunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 
-  if (threadIdx.x < ng) {
-    const int g = threadIdx.x;
+  // per-head max, weight sum and normalised weights (wave per head)
+  for (int g = wave; g < ng; g += 4) {
     float M = neg_inf();
-    for (int cc = 0; cc < nlive; ++cc) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
+    for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float S = 0.f;
-    for (int cc = 0; cc < nlive; ++cc) {
+    for (int cc = lane; cc < nlive; cc += 64) {
       const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
       w[cc][g] = e;
       S += e;
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
     const float invS = 1.0f / S;
-    for (int cc = 0; cc < nlive; ++cc) w[cc][g] *= invS;
-    p.lse_part[orow0 + g] = M + logf(S);
+    for (int cc = lane; cc < nlive; cc += 64) w[cc][g] *= invS;
+    if (lane == 0) p.lse_part[orow0 + g] = M + logf(S);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < ng * (D / 4); e += 256) {
-    const int g = e / (D / 4);
-    const int d = 4 * (e % (D / 4));
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    for (int cc = 0; cc < nlive; ++cc)
-      y += w[cc][g] * *reinterpret_cast<const f32x4*>(p.ws_o + ((slot0 + cc) * p.Gb + g) * D + d);
-    store4(p.o_part, (orow0 + g) * D + d, y, p.odt);
+
+  constexpr int Q = D / 4;               // float4 outputs per head
+  const int E = ng * Q;                  // float4 outputs of this unit
+  int P = 1;                             // chunk partitions
+  while (P < 8 && E * P * 2 <= 256) P *= 2;
+  const int t = threadIdx.x;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  for (int e0 = 0; e0 < E; e0 += 256 / P) {
+    const int e = e0 + t % (256 / P);
+    const int part_id = t / (256 / P);
+    y = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (e < E) {
+      const int g = e / Q;
+      const float* src = p.ws_o + (slot0 * p.Gb + g) * D + 4 * (e % Q);
+      const int64_t cstride = (int64_t)p.Gb * D;
+#pragma unroll 4
+      for (int cc = part_id; cc < nlive; cc += P)
+        y += w[cc][g] * *reinterpret_cast<const f32x4*>(src + cc * cstride);
+    }
+    if (P > 1) {
+      part[t] = y;
+      __syncthreads();
+      if (part_id == 0 && e < E) {
+        for (int q = 1; q < P; ++q) y += part[t + q * (256 / P)];
+      }
+      __syncthreads();
+    }
+    if (part_id == 0 && e < E) store4(p.o_part, (orow0 + e / Q) * D + 4 * (e % Q), y, p.odt);
   }
 }
 

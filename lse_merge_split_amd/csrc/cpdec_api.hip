@@ -70,6 +70,10 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   if ((d->kv_stride_token | d->kv_stride_head | d->kv_stride_batch) % 8 != 0)
     return CPDEC_ERR_ALIGNMENT;
 
+  // K/V of one (shard, sequence, kv head) are addressed with 32-bit offsets.
+  if ((int64_t)(d->kv_capacity > 0 ? d->kv_capacity : 1) * d->kv_stride_token * 2 >= (1ll << 31))
+    return CPDEC_ERR_UNSUPPORTED;
+
   AttnPlan p;
   p.G = d->num_q_heads / d->num_kv_heads;
   p.Gb = p.G < kGroupRows ? p.G : kGroupRows;
@@ -205,6 +209,13 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part, int32_t 
   // Element counts must stay addressable and the grid within 2^31 blocks.
   if (rows > 0 && (uint64_t)rows * (uint64_t)num_shards > (uint64_t)INT64_MAX / 4096)
     return CPDEC_ERR_INVALID_ARG;
+  // Each shard's partial rows, and the lse array, are addressed with 32-bit offsets.
+  {
+    const uint64_t esz = in_dtype == CPDEC_F32 ? 4 : 2;
+    if ((uint64_t)rows * (uint64_t)head_dim * esz >= (1ull << 31) ||
+        (uint64_t)rows * (uint64_t)num_shards * 4 >= (1ull << 31))
+      return CPDEC_ERR_UNSUPPORTED;
+  }
   if (lse_merge_max_blocks(rows, head_dim, in_dtype) > INT32_MAX) return CPDEC_ERR_INVALID_ARG;
   (void)dtype_size;
   if (rows == 0) return CPDEC_OK;

@@ -24,6 +24,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
+// Index of the calling wave in its workgroup, as a value the compiler knows
+// to be wave-uniform (loops over it compile to scalar branches, not exec masks).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---- 16-bit <-> fp32 conversions ------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -75,6 +81,33 @@ constexpr uint32_t kSelLoHalves = 0x05040100u;  // {lo16(hi), lo16(lo)}
 constexpr uint32_t kSelHiHalves = 0x07060302u;  // {hi16(hi), hi16(lo)}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ---- raw buffer loads ---------------------------------------------------
+// A buffer resource covers [base, base + bytes); a load whose offset falls
+// outside returns zeros without touching memory.  Streaming loads go through
+// these intrinsics rather than plain pointer loads: the IR optimiser merges
+// plain loads that feed a loop-carried phi into one load after the phi, which
+// turns a software prefetch back into a load-then-wait; it leaves these alone.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSrdConfig = 0x00020000;  // gfx9 raw buffer: 32-bit format, no swizzle
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any range we build
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kSrdConfig);
+}
+// Cache-policy bits of a buffer load on gfx950: bit 1 = nt (non-temporal).
+constexpr int kPolicyStream = 2;  // data read once: stream it through the caches
+__device__ __forceinline__ u32x4 buf16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 buf16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyStream));
+}
+__device__ __forceinline__ float buf4f(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace cpdec

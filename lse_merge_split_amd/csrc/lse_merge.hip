@@ -7,20 +7,26 @@
 // and converted to FP16/BF16; the merged lse is max lse + ln(sum of weights).
 //
 // Design (HBM-streaming, ~0.5 flop/byte, no MFMA):
-//   * One row group of GS lanes per output row; each lane owns 16-byte
-//     vectors of the row (D=512 bf16: one wave per row, one 16-byte load per
-//     lane per shard; D=128 fp32: two rows per wave).
+//   * One row group of GS lanes per output row, one output row per group and
+//     no persistence: a wave lives for one lse round trip and one round trip
+//     for the partial rows, so many waves fit on a CU and hide the latency
+//     (persistent, software-pipelined forms measured no faster: this access
+//     pattern runs at the memory system's limit for 8 strided read streams
+//     plus a write stream).  Each lane owns 16-byte vectors of the row (D=512
+//     16-bit: one wave per row, one 16-byte load per lane per shard).
 //   * Weights are formed in FP64 so the merged lse keeps ~1e-7 relative
-//     accuracy even when it cancels towards 0.  Lane j of a row group computes
-//     the one exp of shard j and the weights reach the other lanes by shuffles;
-//     the weight sum (FP64) and the o sum (FP32) run in shard order, and the
-//     division by the weight sum is applied once at the end.
-//   * Shards with lse = -inf are skipped before their row is loaded: their
-//     bytes are never read and any garbage/NaN in them cannot leak.
-//   * Loads of a batch of 8 shards are issued back to back before any use so
-//     8 x 16 bytes per lane are in flight.  For R <= 8 a persistent,
-//     software-pipelined form overlaps the next row's lse fetch with this
-//     row's partial loads; larger R uses one wave per row and batches of 8.
+//     accuracy even when it cancels towards 0.  Lane j computes the one exp of
+//     shard j while the partial rows load; shuffles (or readlane when a wave
+//     holds one row) hand the weights to the other lanes.  The weight sum
+//     (FP64) and the o sum (FP32) run in shard order, and the division by the
+//     weight sum is applied once at the end.
+//   * Shards with lse = -inf are skipped before their row is loaded: the load
+//     is given an offset outside its buffer resource, which returns zeros
+//     without touching memory, so their bytes are never read and garbage/NaN
+//     in them cannot leak.
+//   * Partial rows are read through buffer loads with the non-temporal
+//     (streaming) policy; batches of 8 shards keep 8 x 16 bytes per lane in
+//     flight.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -73,6 +79,12 @@ template <> __device__ __forceinline__ void store_vec<f16_t, 8>(f16_t* p, const 
 constexpr int kMergeWaves = 4;
 constexpr int kBatch = 8;  // shards whose loads are in flight together
 
+// One row per row group, non-persistent (a wave's whole life is one memory
+// round trip for the lse values and one for the partial rows, so many waves
+// fit on a CU).  Lane li of a row group owns shards li, li + GS, ...: it
+// loads their lse, the group takes the max, then every live shard's row is
+// requested before the FP64 exps are computed, so the arithmetic overlaps the
+// loads.  Batches of kBatch shards keep 8 x 16 bytes per lane in flight.
 template <typename Tin, typename Tout, int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
     const Tin* __restrict__ o, const float* __restrict__ lse, int R, int64_t rows,
@@ -85,16 +97,17 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   static_assert(NV % GS == 0 && 64 % GS == 0 && GS >= kBatch, "row split");
 
   const int lane = threadIdx.x & 63;
-  const int64_t row_raw = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW + lane / GS;
+  const int64_t row_raw = ((int64_t)blockIdx.x * kMergeWaves + wave_id()) * RPW + lane / GS;
   const bool valid = row_raw < rows;
   const int64_t row = valid ? row_raw : rows - 1;  // idle lanes shadow a real row
   const int li = lane % GS;
-  const int base = lane - li;                      // first lane of this row group
-  const float* lrow = lse + row;
+  const int base = lane - li;
+  const rsrc_t lrs = make_rsrc(lse, (uint32_t)((int64_t)R * rows * sizeof(float)));
+  const uint32_t roff = (uint32_t)(row * D * sizeof(Tin)) + (uint32_t)(li * 16);
 
   // Row max over shards: lane li reads shards li, li+GS, ..., then the group reduces.
   float M = neg_inf();
-  for (int r = li; r < R; r += GS) M = fmaxf(M, lrow[(int64_t)r * rows]);
+  for (int r = li; r < R; r += GS) M = fmaxf(M, buf4f(lrs, (uint32_t)(((int64_t)r * rows + row) * 4)));
 #pragma unroll
   for (int off = GS / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, GS));
 
@@ -117,31 +130,33 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[v][e] = 0.f;
 
-  const Tin* obase = o + row * D + li * VEC;
   for (int rb = 0; rb < R; rb += GS) {
-    // one FP64 exp per lane: lane li owns shard rb + li of this block
+    // lane li owns shard rb + li of this block (its lse is cached from above)
     const int rl = rb + li;
-    const float lme = (rl < R) ? lrow[(int64_t)rl * rows] : neg_inf();
-    const double eme = (lme != neg_inf()) ? exp((double)lme - Md) : 0.0;
+    const float lme = (rl < R) ? buf4f(lrs, (uint32_t)(((int64_t)rl * rows + row) * 4)) : neg_inf();
     const int nb = min(GS, R - rb);
     for (int j0 = 0; j0 < nb; j0 += kBatch) {
-      double e[kBatch];
+      float lj[kBatch];
       u32x4 raw[kBatch][VPL];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int src = base + ((j0 + j) < nb ? (j0 + j) : 0);
-        e[j] = (j0 + j < nb) ? __shfl(eme, src) : 0.0;
-        if (e[j] != 0.0) {  // empty shards (and weights below FP64 range) are never read
-          const Tin* sp = obase + (int64_t)(rb + j0 + j) * rows * D;
+        const float l = __shfl(lme, base + min(j0 + j, nb - 1));
+        lj[j] = (j0 + j < nb) ? l : neg_inf();
+        // an empty shard's row is never read: its offset is out of range (zeros)
+        const rsrc_t ors = make_rsrc(o + (int64_t)(rb + min(j0 + j, nb - 1)) * rows * D,
+                                     (uint32_t)(rows * D * sizeof(Tin)));
+        const uint32_t off = (lj[j] != neg_inf()) ? roff : kOutOfRange;
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(sp + v * GS * VEC);
-        }
+        for (int v = 0; v < VPL; ++v) raw[j][v] = buf16_stream(ors, off + (uint32_t)(v * GS * 16));
       }
+      // the exps of this batch's shards, computed while the rows load
+      const double e_own = (lme != neg_inf()) ? exp((double)lme - Md) : 0.0;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        if (e[j] == 0.0) continue;
-        S += e[j];
-        const float wj = (float)e[j];
+        const double ej = __shfl(e_own, base + min(j0 + j, nb - 1));
+        if (lj[j] == neg_inf() || ej == 0.0) continue;  // never read, never used
+        S += ej;
+        const float wj = (float)ej;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
           float x[VEC];
@@ -165,122 +180,86 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   if (lse_out != nullptr && li == 0) lse_out[row] = (float)(Md + log(S));
 }
 
-// Pipelined form for R <= kBatch (every shard's 16-byte vectors in flight
-// together): persistent waves walk rows with a stride; while the partial rows
-// of row k are loading, the lse values of row k+1 are already requested, so a
-// row costs one memory round trip.  Lane li of a row group owns shard li's lse
-// and its FP64 exp; shuffles hand the values to the other lanes.
+// R <= kBatch and a whole wave per row (e.g. D = 512 in 16-bit types): the
+// row index is wave-uniform, so the lse values arrive through scalar loads
+// (scalar cache; the vector memory pipe carries only the partial rows), lane
+// j computes shard j's FP64 exp and readlane makes every weight uniform.
 template <typename Tin, typename Tout, int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_pipelined_kernel(
+__global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_wave_row_kernel(
     const Tin* __restrict__ o, const float* __restrict__ lse, int R, int64_t rows,
     Tout* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int VEC = InVec<Tin>::N;
   constexpr int NV = D / VEC;
-  constexpr int GS = NV < 64 ? NV : 64;
-  constexpr int RPW = 64 / GS;
-  constexpr int VPL = NV / GS;
-  static_assert(GS >= kBatch, "a row group must hold one lane per shard");
-
+  constexpr int VPL = NV / 64;
+  static_assert(NV % 64 == 0, "one wave per row");
   const int lane = threadIdx.x & 63;
-  const int li = lane % GS;
-  const int base = lane - li;
-  const int64_t step = (int64_t)gridDim.x * kMergeWaves * RPW;
-  int64_t wrow = ((int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6)) * RPW;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + wave_id();  // wave-uniform
+  if (row >= rows) return;
 
-  float l_next = neg_inf();
-  {
-    const int64_t row = wrow + lane / GS;
-    if (row < rows && li < R) l_next = lse[(int64_t)li * rows + row];
+  float lj[kBatch];
+  float M = neg_inf();
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    lj[j] = (j < R) ? lse[(int64_t)j * rows + row] : neg_inf();  // scalar loads
+    M = fmaxf(M, lj[j]);
   }
-  for (; wrow < rows; wrow += step) {
-    const int64_t row = wrow + lane / GS;
-    const bool valid = row < rows;
-    const float l_own = l_next;
-
-    // every shard's lse in every lane of the group; issue the live rows' loads
-    float lj[kBatch];
-    u32x4 raw[kBatch][VPL];
-    const Tin* obase = o + (valid ? row : 0) * D + li * VEC;
+  Tout* orow = out + row * D;
+  if (M == neg_inf()) {  // every shard empty
+    float z[VEC] = {};
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      lj[j] = __shfl(l_own, base + j);
-      if (j >= R) lj[j] = neg_inf();
-      if (valid && lj[j] != neg_inf()) {
-        const Tin* sp = obase + (int64_t)j * rows * D;
+    for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * 64 + lane) * VEC, z);
+    if (lse_out != nullptr && lane == 0) lse_out[row] = neg_inf();
+    return;
+  }
+  const uint32_t roff = (uint32_t)(row * D * sizeof(Tin)) + (uint32_t)(lane * 16);
+  u32x4 raw[kBatch][VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) raw[j][v] = ld16(sp + v * GS * VEC);
-      }
-    }
-    // request the next row's lse while these loads are in flight
-    {
-      const int64_t nrow = row + step;
-      l_next = (nrow < rows && li < R) ? lse[(int64_t)li * rows + nrow] : neg_inf();
-    }
-
-    float M = lj[0];
+  for (int j = 0; j < kBatch; ++j) {
+    const rsrc_t ors = make_rsrc(o + (int64_t)(j < R ? j : 0) * rows * D, (uint32_t)(rows * D * sizeof(Tin)));
+    // an empty shard's row is never read: its offset is out of range (zeros)
+    const uint32_t off = (lj[j] != neg_inf()) ? roff : kOutOfRange;
 #pragma unroll
-    for (int j = 1; j < kBatch; ++j) M = fmaxf(M, lj[j]);
-    Tout* orow = out + (valid ? row : 0) * D;
-    if (M == neg_inf()) {  // every shard empty
-      if (valid) {
-        float z[VEC] = {};
+    for (int v = 0; v < VPL; ++v) raw[j][v] = buf16_stream(ors, off + (uint32_t)(v * 64 * 16));
+  }
+  // lane j: shard j's weight in FP64, while the rows load
+  float lmine = neg_inf();
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, z);
-        if (lse_out != nullptr && li == 0) lse_out[row] = neg_inf();
-      }
-      continue;
-    }
-    const double Md = (double)M;
-    const double e_own = (l_own != neg_inf() && li < R) ? exp((double)l_own - Md) : 0.0;
-    double S = 0.0;
-    float acc[VPL][VEC];
+  for (int j = 0; j < kBatch; ++j) lmine = (lane == j) ? lj[j] : lmine;
+  const double Md = (double)M;
+  const double e_mine = (lmine != neg_inf()) ? exp((double)lmine - Md) : 0.0;
+  double S = 0.0;
+  float acc[VPL][VEC];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+  for (int v = 0; v < VPL; ++v)
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) acc[v][k] = 0.f;
+    for (int k = 0; k < VEC; ++k) acc[v][k] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const double ej = __shfl(e_own, base + j);
-      if (lj[j] == neg_inf() || ej == 0.0) continue;
-      S += ej;
-      const float wj = (float)ej;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        float x[VEC];
-        InVec<Tin>::cvt(raw[j][v], x);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(wj, x[k], acc[v][k]);
-      }
-    }
-    if (!valid) continue;
-    const float inv = (float)(1.0 / S);
+  for (int j = 0; j < kBatch; ++j) {
+    const double ej = __builtin_bit_cast(
+        double, ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane(
+                     (int)(__builtin_bit_cast(unsigned long long, e_mine) >> 32), j) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane(
+                        (int)__builtin_bit_cast(unsigned long long, e_mine), j));
+    if (lj[j] == neg_inf() || ej == 0.0) continue;  // uniform branch
+    S += ej;
+    const float wj = (float)ej;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      float y[VEC];
+      float x[VEC];
+      InVec<Tin>::cvt(raw[j][v], x);
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) y[k] = acc[v][k] * inv;
-      store_vec<Tout, VEC>(orow + (v * GS + li) * VEC, y);
+      for (int k = 0; k < VEC; ++k) acc[v][k] = fmaf(wj, x[k], acc[v][k]);
     }
-    if (lse_out != nullptr && li == 0) lse_out[row] = (float)(Md + log(S));
   }
-}
-
-// Resident workgroups per CU x CUs for a kernel on the current device
-// (queried once per device and kernel; a benign race recomputes the same value).
-template <typename K>
-int64_t resident_blocks(K kernel, int threads) {
-  static int64_t cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-  if (cache[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 1024;
-    cache[dev] = (int64_t)cus * per_cu;
+  const float inv = (float)(1.0 / S);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    float y[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) y[k] = acc[v][k] * inv;
+    store_vec<Tout, VEC>(orow + (v * 64 + lane) * VEC, y);
   }
-  return cache[dev];
+  if (lse_out != nullptr && lane == 0) lse_out[row] = (float)(Md + log(S));
 }
 
 template <typename Tin, typename Tout, int D>
@@ -288,18 +267,18 @@ hipError_t launch_typed(const void* o, const float* lse, int R, int64_t rows, vo
                         float* lse_out, hipStream_t s) {
   constexpr int VEC = InVec<Tin>::N;
   constexpr int NV = D / VEC;
+  if constexpr (NV % 64 == 0) {
+    if (R <= kBatch) {  // a whole wave per row: scalar lse loads
+      const int64_t blocks = (rows + kMergeWaves - 1) / kMergeWaves;
+      hipLaunchKernelGGL((lse_merge_wave_row_kernel<Tin, Tout, D>), dim3((unsigned)blocks),
+                         dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
+                         static_cast<Tout*>(out), lse_out);
+      return hipGetLastError();
+    }
+  }
   constexpr int GS = NV < 64 ? NV : 64;
   constexpr int rows_per_block = kMergeWaves * (64 / GS);
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  if (blocks == 0) return hipSuccess;
-  if (R <= kBatch) {
-    auto kern = lse_merge_pipelined_kernel<Tin, Tout, D>;
-    int64_t grid = resident_blocks(kern, kMergeWaves * 64);
-    if (grid > blocks) grid = blocks;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMergeWaves * 64), 0, s,
-                       static_cast<const Tin*>(o), lse, R, rows, static_cast<Tout*>(out), lse_out);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D>), dim3((unsigned)blocks),
                      dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
                      static_cast<Tout*>(out), lse_out);
