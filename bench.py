@@ -12,10 +12,12 @@ Prints ONE JSON line:
                  steps launched from Python / K)
   roofline       the dominant kernel (attention; the merge for c5):
                  algorithmic bytes per launch / its mean duration from HIP
-                 events recorded around each launch inside the timed region,
-                 against MI355X's 8 TB/s HBM peak; `traffic` is filled from
-                 the committed rocprofv3 counter summary when it was taken
-                 on the current kernel source, else null
+                 events recorded around its launches on every 8th step of the
+                 timed region, against MI355X's 8 TB/s HBM peak (for split
+                 workloads the attention span includes its chunk-merge
+                 kernel); `traffic` is filled from the committed rocprofv3
+                 counter summary when it was taken on the current kernel
+                 source, else null
   cpu_baseline   the CPU oracle timed on this host on a bounded sample of the
                  same workload, scaled to microseconds per call
 
@@ -233,15 +235,17 @@ def main():
     print(f"[bench] workload {w.name}: {w.note}; copies={info['copies']} steps={K} warmup={W}",
           file=sys.stderr, flush=True)
 
+    stream = torch.cuda.current_stream().cuda_stream  # every call goes on this stream
+
     def step(i, ev=None):
         a, m = steps[i % len(steps)]
-        if ev is not None:
-            ev[0].record()
         if a is not None:
-            a()
+            if ev is not None:
+                ev[0].record()
+            a(stream)
         if ev is not None:
             ev[1].record()
-        m()
+        m(stream)
         if ev is not None:
             ev[2].record()
 
@@ -249,19 +253,28 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # HIP events bracket the kernels of every EVERY-th timed step (each event
+    # record costs a few microseconds of device time, so bracketing every step
+    # would inflate the per-step time of the small workloads).
+    EVERY = 8
+    sampled = list(range(0, K, EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    edge[0].record()
     for i in range(K):
-        step(i, evs[i])
+        step(i, evs.get(i))
+    edge[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
 
     us_per_call = (t1 - t0) / K * 1e6
-    attn_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    merge_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
-    device_us = evs[0][0].elapsed_time(evs[-1][2]) * 1e3 / K
+    attn_us = (float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])) * 1e3
+               if not w.merge_only else None)
+    merge_us = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])) * 1e3
+    device_us = edge[0].elapsed_time(edge[1]) * 1e3 / K
 
     if w.merge_only:
         dom_name, dom_us, dom_bytes, kernel = "lse_merge_kernel", merge_us, alg_merge, "lse_merge"
@@ -278,9 +291,10 @@ def main():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream  # the capture stream
                 if a is not None:
-                    a()
-                m()
+                    a(cs)
+                m(cs)
         torch.cuda.synchronize()
         for _ in range(W):
             g.replay()
@@ -325,12 +339,14 @@ def main():
                    "rows": w.rows or None, "input_copies": info["copies"],
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
                    "waves_per_workgroup": info.get("waves"), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or info.get("nchunks", 1) == 1
+                                                           else " + attn_combine_kernel"),
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
-                     "mean_launch_us": round(dom_us, 3)},
+                     "mean_launch_us": round(dom_us, 3), "event_samples": len(sampled)},
         "cpu_baseline": cpu,
-        "attn_us": round(attn_us, 3) if not w.merge_only else None,
+        "attn_us": round(attn_us, 3) if attn_us is not None else None,
         "merge_us": round(merge_us, 3),
         "device_us_per_call": round(device_us, 3),
         "graph_us_per_call": round(graph_us, 3) if graph_us is not None else None,

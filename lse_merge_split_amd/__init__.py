@@ -183,11 +183,13 @@ class AttnCall:
         self._args = [ctypes.byref(desc), q.data_ptr(), ks, vs, lens.data_ptr(), o_part.data_ptr(),
                       lse_part.data_ptr(), ws_ptr, ws_bytes]
         self._arrays = (ks, vs)
+        self._fn = lib().cpdec_attn_partial
 
     def __call__(self, stream=None):
-        torch = _torch()
-        s = stream if stream is not None else torch.cuda.current_stream(self._device).cuda_stream
-        rc = lib().cpdec_attn_partial(*self._args, s)
+        """Enqueue on `stream` (a hipStream_t handle), else torch's current stream."""
+        if stream is None:
+            stream = _torch().cuda.current_stream(self._device).cuda_stream
+        rc = self._fn(*self._args, stream)
         if rc != 0:
             raise CpdecError(rc, "cpdec_attn_partial")
 
@@ -212,11 +214,13 @@ class MergeCall:
         self._args = [o_part.data_ptr(), lse_part.data_ptr(), R, rows, D, dtype_code(o_part.dtype),
                       dtype_code(out.dtype), out.data_ptr(),
                       lse_out.data_ptr() if lse_out is not None else None]
+        self._fn = lib().cpdec_lse_merge
 
     def __call__(self, stream=None):
-        torch = _torch()
-        s = stream if stream is not None else torch.cuda.current_stream(self._device).cuda_stream
-        rc = lib().cpdec_lse_merge(*self._args, s)
+        """Enqueue on `stream` (a hipStream_t handle), else torch's current stream."""
+        if stream is None:
+            stream = _torch().cuda.current_stream(self._device).cuda_stream
+        rc = self._fn(*self._args, stream)
         if rc != 0:
             raise CpdecError(rc, "cpdec_lse_merge")
 
