@@ -1,0 +1,71 @@
+"""HIP-graph replay of a whole step (partial attention + merge) gives the
+eager result bit for bit on every replay, with eager work and
+synchronisations between replays (the path records no memset nodes)."""
+import sys
+
+import pytest
+
+from synth import configs as sc
+from tests.helpers import run_path
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+import lse_merge_split_amd as cp  # noqa: E402
+from synth import gpu as sg  # noqa: E402
+
+
+@pytest.mark.parametrize("name,w", [
+    ("split shards (chunk merge)", sc.small("c4", B=8, Lcap=700)),
+    ("whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
+    ("merge-only rows", None),
+])
+def test_graph_replay_matches_eager(name, w):
+    print(f"[case] graph replay: {name}", flush=True)
+    sys.stdout.flush()
+    if w is None:
+        wm = sc.WORKLOADS["c5"].scaled(rows=4096)
+        inp = sg.merge_inputs(wm)
+        out = torch.empty((wm.rows, wm.D), dtype=torch.bfloat16, device="cuda")
+        lo = torch.empty(wm.rows, dtype=torch.float32, device="cuda")
+        calls = [cp.MergeCall(inp["o_part"], inp["lse_part"], out, lo)]
+        outs = [out, lo]
+        ref_out, ref_lo = torch.empty_like(out), torch.empty_like(lo)
+        cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
+        refs = [ref_out, ref_lo]
+        eager_work = lambda: cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
+    else:
+        inp = sg.attn_inputs(w)
+        ref = run_path(inp)
+        R, B, Hq, D = w.R, w.B, w.Hq, w.D
+        o_part = torch.empty((R, B, Hq, D), dtype=torch.float32, device="cuda")
+        lse_part = torch.empty((R, B, Hq), dtype=torch.float32, device="cuda")
+        out = torch.empty((B, Hq, D), dtype=inp["q"].dtype, device="cuda")
+        lo = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(256, cp.attn_workspace_bytes(cp.make_attn_desc(inp["q"], inp["k_shards"]))),
+                         dtype=torch.uint8, device="cuda")
+        calls = [cp.AttnCall(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], o_part, lse_part,
+                             workspace=ws),
+                 cp.MergeCall(o_part, lse_part, out, lo)]
+        outs = [o_part, lse_part, out, lo]
+        refs = [ref["o_part"], ref["lse_part"], ref["out"], ref["lse_out"]]
+        eager_work = lambda: run_path(inp)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for c in calls:
+                c(cs)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan") if t.dtype.is_floating_point else 0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, refs):
+            assert torch.equal(t, r), f"replay {rep}: output differs from eager"
+        eager_work()
+        torch.cuda.synchronize()
