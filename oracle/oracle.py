@@ -98,6 +98,30 @@ def merge(o_parts: np.ndarray, lse_parts: np.ndarray):
     return out, lse_out
 
 
+def round_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Values of x after storing them as fp16 or bf16 (round to nearest even),
+    returned as float64.  Used for partials that travel in 16 bits.
+
+    bf16 keeps the top 16 bits of the float32 pattern; rounding adds half an
+    ulp plus the tie-to-even bit before truncating.  x is first rounded to
+    float32 (exact for every value the merge produces in float32)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "fp16":
+        return x32.astype(np.float16).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def merge_stored(o_parts: np.ndarray, lse_parts: np.ndarray, dtype: str):
+    """The merge of partials that were stored in 16 bits on their way (what a
+    context-parallel exchange carries when its payload is fp16/bf16): the
+    exact partials rounded to the storage type, then merged exactly."""
+    return merge(round_storage(o_parts, dtype), lse_parts)
+
+
 def merge_rows(o_parts: np.ndarray, lse_parts: np.ndarray):
     """``merge`` applied row by row.  o_parts [R, N, D], lse_parts [R, N]."""
     R, N, D = o_parts.shape

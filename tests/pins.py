@@ -251,6 +251,31 @@ def pin_merge_all_empty(impl):
     assert np.array_equal(out, np.zeros(4)) and l == -INF
 
 
+def pin_round_storage(impl):
+    """16-bit storage rounding: exact values unchanged, ties to even, the
+    fp16 range and the bf16 ulp of 1 (2^-7)."""
+    if not hasattr(impl, "round_storage"):
+        return
+    rs = impl.round_storage
+    exact = np.array([1.0, -2.5, 0.15625, 3.0 * 2.0 ** -20])
+    assert np.array_equal(rs(exact, "bf16"), exact) and np.array_equal(rs(exact, "fp16"), exact)
+    assert rs(np.array([1.0 + 2.0 ** -8]), "bf16")[0] == 1.0            # tie -> even
+    assert rs(np.array([1.0 + 3 * 2.0 ** -8]), "bf16")[0] == 1.0 + 2.0 ** -6  # tie -> even (up)
+    assert rs(np.array([1.0 + 2.0 ** -8 + 2.0 ** -12]), "bf16")[0] == 1.0 + 2.0 ** -7
+    assert rs(np.array([1.0 + 2.0 ** -11]), "fp16")[0] == 1.0            # fp16 tie -> even
+    assert rs(np.array([1.0 + 2.0 ** -10]), "fp16")[0] == 1.0 + 2.0 ** -10
+    rng = _rng(16)
+    x = rng.normal(size=1000)
+    for dt, ulp in (("bf16", 2.0 ** -8), ("fp16", 2.0 ** -11)):
+        y = rs(x, dt)
+        assert np.all(np.abs(y - x) <= ulp * np.abs(x) + 1e-30)
+        assert np.array_equal(rs(y, dt), y)                              # idempotent
+    o = rng.normal(size=(3, 5))
+    out, l = impl.merge_stored(o, np.array([0.0, 1.0, -1.0]), "bf16")
+    out2, l2 = impl.merge(rs(o, "bf16"), np.array([0.0, 1.0, -1.0]))
+    assert np.array_equal(out, out2) and l == l2
+
+
 # --------------------------------------------------------------- whole-path pins
 def _random_split_problem(rng, B, Hq, Hkv, D, R, Lmax, empty_p=0.2):
     lens = rng.integers(0, Lmax + 1, size=(R, B))
@@ -332,7 +357,8 @@ ATTEND_PINS = [pin_textbook_bruteforce, pin_single_token, pin_uniform_scores,
                pin_large_scores_stable, pin_empty_shard, pin_library_sdpa]
 MERGE_PINS = [pin_merge_single_shard_identity, pin_merge_equal_lse, pin_merge_dominant,
               pin_merge_two_by_hand, pin_merge_shift, pin_merge_bounds,
-              pin_merge_permutation, pin_merge_empty_shard, pin_merge_all_empty]
+              pin_merge_permutation, pin_merge_empty_shard, pin_merge_all_empty,
+              pin_round_storage]
 PATH_PINS = [pin_split_invariance, pin_gqa_mapping, pin_default_scale,
              pin_partials_are_per_shard]
 ALL_PINS = ATTEND_PINS + MERGE_PINS + PATH_PINS

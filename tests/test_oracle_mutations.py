@@ -39,6 +39,10 @@ MUTATIONS = [
     ("all-empty lse 0", "return np.zeros(D), NEG_INF", "return np.zeros(D), 0.0"),
     ("default scale 1/D", "scale = 1.0 / math.sqrt(D)\n    o_part",
      "scale = 1.0 / D\n    o_part"),
+    ("bf16 rounding truncates", "(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1)))",
+     "(u)"),
+    ("bf16 rounding without ties-to-even", "(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1)))",
+     "(u + np.uint64(0x8000))"),
 ]
 
 
