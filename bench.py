@@ -74,7 +74,7 @@ def merge_alg_bytes(R: int, rows: int, D: int, live: int, in_elem: int, out_elem
 
 
 # ------------------------------------------------------------------ GPU setup
-def build_attn_steps(w: sc.Workload, torch, cp, sg):
+def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = False):
     inp = sg.attn_inputs(w)
     lens = inp["lens_np"]
     per_copy = 2 * inp["k"].numel() * inp["k"].element_size()
@@ -92,8 +92,13 @@ def build_attn_steps(w: sc.Workload, torch, cp, sg):
     lse_out = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
     steps = []
     for s in sets:
-        a = cp.AttnCall(s["q"], s["k_shards"], s["v_shards"], s["lens"], o_part, lse_part)
-        m = cp.MergeCall(o_part, lse_part, out, lse_out)
+        if fused:  # cpdec_cp_decode: the whole step as one call (two launches)
+            a = cp.StepCall(s["q"], s["k_shards"], s["v_shards"], s["lens"], o_part, lse_part,
+                            out, lse_out)
+            m = None
+        else:
+            a = cp.AttnCall(s["q"], s["k_shards"], s["v_shards"], s["lens"], o_part, lse_part)
+            m = cp.MergeCall(o_part, lse_part, out, lse_out)
         steps.append((a, m))
     alg_attn = attn_alg_bytes(w, lens)
     live_rows = int((np.repeat(lens[:, :, None] > 0, w.Hq, axis=2)).sum())
@@ -209,6 +214,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--graph", action="store_true", help="also time HIP-graph replay of a step")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the whole step as one cpdec_cp_decode call instead of "
+                         "cpdec_attn_partial + cpdec_lse_merge")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy after the timed region (counter scaling)")
     args = ap.parse_args()
@@ -228,7 +236,7 @@ def main():
         steps, alg_attn, alg_merge, info = build_merge_steps(w, torch, cp, sg)
         K = args.steps or 100
     else:
-        steps, alg_attn, alg_merge, info = build_attn_steps(w, torch, cp, sg)
+        steps, alg_attn, alg_merge, info = build_attn_steps(w, torch, cp, sg, fused=args.fused)
         K = args.steps or (200 if alg_attn < (1 << 30) else 20)
     W = args.warmup
     torch.cuda.synchronize()
@@ -245,7 +253,8 @@ def main():
             a(stream)
         if ev is not None:
             ev[1].record()
-        m(stream)
+        if m is not None:
+            m(stream)
         if ev is not None:
             ev[2].record()
 
@@ -273,11 +282,15 @@ def main():
     us_per_call = (t1 - t0) / K * 1e6
     attn_us = (float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])) * 1e3
                if not w.merge_only else None)
-    merge_us = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])) * 1e3
+    merge_us = (float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])) * 1e3
+                if not args.fused else None)
     device_us = edge[0].elapsed_time(edge[1]) * 1e3 / K
 
     if w.merge_only:
         dom_name, dom_us, dom_bytes, kernel = "lse_merge_kernel", merge_us, alg_merge, "lse_merge"
+    elif args.fused:  # the event span covers the whole step (attention + fused merge)
+        dom_name, dom_us, dom_bytes, kernel = ("attn_partial_kernel + attn_combine_merge_kernel",
+                                               attn_us, alg_attn + alg_merge, "attn_partial")
     else:
         dom_name, dom_us, dom_bytes, kernel = "attn_partial_kernel", attn_us, alg_attn, "attn_partial"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -294,7 +307,8 @@ def main():
                 cs = torch.cuda.current_stream().cuda_stream  # the capture stream
                 if a is not None:
                     a(cs)
-                m(cs)
+                if m is not None:
+                    m(cs)
         torch.cuda.synchronize()
         for _ in range(W):
             g.replay()
@@ -334,12 +348,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f16",
         "data": "synthetic (seeded Philox streams; no dataset)",
-        "config": {"workload": f"{w.name}: {w.note}", "R": w.R, "B": w.B or None,
+        "config": {"workload": f"{w.name}: {w.note}", "entry": ("cpdec_cp_decode" if args.fused else
+                                                          "cpdec_attn_partial + cpdec_lse_merge"),
+                   "R": w.R, "B": w.B or None,
                    "Hq": w.Hq or None, "Hkv": w.Hkv or None, "D": w.D,
                    "rows": w.rows or None, "input_copies": info["copies"],
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
                    "waves_per_workgroup": info.get("waves"), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or info.get("nchunks", 1) == 1
+        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or args.fused
+                                                           or info.get("nchunks", 1) == 1
                                                            else " + attn_combine_kernel"),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -347,7 +364,7 @@ def main():
                      "mean_launch_us": round(dom_us, 3), "event_samples": len(sampled)},
         "cpu_baseline": cpu,
         "attn_us": round(attn_us, 3) if attn_us is not None else None,
-        "merge_us": round(merge_us, 3),
+        "merge_us": round(merge_us, 3) if merge_us is not None else None,
         "device_us_per_call": round(device_us, 3),
         "graph_us_per_call": round(graph_us, 3) if graph_us is not None else None,
         "step_alg_bytes": step_bytes,

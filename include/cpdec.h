@@ -173,6 +173,31 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
                              void* out, float* lse_out, void* stream);
 
 /*
+ * The whole step in two launches: cpdec_attn_partial's partials (written to
+ * o_part/lse_part exactly as that call writes them) and their LSE merge into
+ * out/lse_out, with the merge formula of cpdec_lse_merge (page sections
+ * "Introduction" and "Code analysis, 1. Fused kernel").  When shards are split
+ * into chunks the per-shard chunk merge and the cross-shard merge share one
+ * kernel (one launch fewer than the two calls); otherwise the second launch is
+ * cpdec_lse_merge itself.  The cross-shard sum runs as an online merge in
+ * shard order, so `out` agrees with cpdec_lse_merge of the same partials to
+ * rounding, not bit for bit, in the split case.
+ *
+ *   d, q, k_shards, v_shards, lens, o_part, lse_part, workspace,
+ *   workspace_bytes, stream   as for cpdec_attn_partial
+ *   out        device, [B][Hq][D] in qkv_dtype, 16-byte aligned
+ *   lse_out    device, float [B][Hq], or NULL to skip writing it
+ * Errors: as cpdec_attn_partial; INVALID_ARG for a NULL out; ALIGNMENT for a
+ * misaligned out or lse_out.
+ */
+cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
+                             const void* const* k_shards,
+                             const void* const* v_shards, const int32_t* lens,
+                             void* o_part, float* lse_part, void* out,
+                             float* lse_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Zero-fill `bytes` bytes of a buffer on `stream` with a kernel (no
  * hipMemset, so it is safe to record in a HIP graph).  Workspaces do not need
  * it; it is offered for callers that want deterministic buffer contents.

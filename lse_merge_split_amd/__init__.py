@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "attn_partial", "lse_merge",
+__all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "StepCall", "attn_partial",
+           "lse_merge", "cp_decode",
            "attn_workspace_bytes", "attn_plan", "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
         L.cpdec_attn_partial.restype = ctypes.c_int
+        L.cpdec_cp_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
+                                      ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cpdec_cp_decode.restype = ctypes.c_int
         L.cpdec_lse_merge.argtypes = [vp, vp, i32, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.cpdec_lse_merge.restype = ctypes.c_int
         L.cpdec_workspace_clear.argtypes = [vp, sz, vp]
@@ -192,6 +196,37 @@ class AttnCall:
         rc = self._fn(*self._args, stream)
         if rc != 0:
             raise CpdecError(rc, "cpdec_attn_partial")
+
+
+class StepCall(AttnCall):
+    """A cpdec_cp_decode call (the whole step: partials and their merge, two
+    launches) with its arguments marshalled once."""
+
+    def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, **kw):
+        super().__init__(q, k_shards, v_shards, lens, o_part, lse_part, **kw)
+        if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, Hq, D] tensor of q's dtype")
+        if lse_out is not None and (tuple(lse_out.shape) != tuple(q.shape[:2])
+                                    or not lse_out.is_contiguous()):
+            raise ValueError("lse_out must be a contiguous [B, Hq] float32 tensor")
+        self._keep = self._keep + (out, lse_out)
+        a = self._args
+        self._args = a[:7] + [out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None] + a[7:]
+        self._fn = lib().cpdec_cp_decode
+
+    def __call__(self, stream=None):
+        if stream is None:
+            stream = _torch().cuda.current_stream(self._device).cuda_stream
+        rc = self._fn(*self._args, stream)
+        if rc != 0:
+            raise CpdecError(rc, "cpdec_cp_decode")
+
+
+def cp_decode(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, *, stream=None,
+              **kw):
+    """Whole step: per-shard partials into o_part/lse_part and their merge into out/lse_out."""
+    StepCall(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out, **kw)(
+        _stream_handle(stream))
 
 
 class MergeCall:

@@ -90,6 +90,14 @@ __device__ __forceinline__ void store4(void* base, int64_t idx, f32x4 x, int odt
   }
 }
 
+// Load 4 consecutive values of dtype `odt` as fp32.
+__device__ __forceinline__ f32x4 load4(const void* base, int64_t idx, int odt) {
+  if (odt == kF32) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+  const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + idx);
+  if (odt == kBF16) return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+  return f32x4{f16_lo(w[0]), f16_hi(w[0]), f16_lo(w[1]), f16_hi(w[1])};
+}
+
 template <int D, int NW>
 struct Smem {
   static constexpr int NB = (D / 8 + 15) / 16;
@@ -420,34 +428,181 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
 }
 
+// The whole step's second launch: for one (sequence, kv head, head block)
+// merge each shard's chunk partials into o_part/lse_part (as
+// attn_combine_kernel does; shards that fit one chunk were written by the
+// attention kernel and are read back), then merge the shards into out/lse_out
+// with an online LSE merge in shard order (FP64 weight sum, FP32 output
+// sum; -inf shards are skipped, so they cannot leak).
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_merge_kernel(const AttnParams p, void* out,
+                                                                 float* lse_out, int out_dt) {
+  __shared__ float w[kMaxChunks][16];
+  __shared__ f32x4 part[256];
+  __shared__ float s_lse[16];
+  const int bh = blockIdx.x;  // ((b * Hkv) + h) * gblocks + gb
+  const int gb = bh % p.gblocks;
+  const int h = (bh / p.gblocks) % p.Hkv;
+  const int b = bh / (p.gblocks * p.Hkv);
+  const int g0 = gb * kGroupRows;
+  const int ng = min(kGroupRows, p.G - g0);
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int t = threadIdx.x;
+
+  constexpr int Q = D / 4;               // float4 outputs per head
+  const int E = ng * Q;                  // float4 outputs of this head block
+  int P = 1;                             // chunk partitions
+  while (P < 8 && E * P * 2 <= 256) P *= 2;
+  const int per = 256 / P;
+  constexpr int kRounds = (kGroupRows * (D / 4) + 255) / 256;  // element rounds per thread (<= 4)
+  const int nrounds = (E + per - 1) / per;
+
+  // running cross-shard state per owned element (partition 0 only): head max,
+  // FP64 weight sum and FP32 output sum
+  float Mrun[kRounds];
+  double Srun[kRounds];
+  f32x4 acc[kRounds];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    Mrun[k] = neg_inf();
+    Srun[k] = 0.0;
+    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int r = 0; r < p.R; ++r) {
+    const int unit = ((r * p.B + b) * p.Hkv + h) * p.gblocks + gb;
+    const int L = p.lens[r * p.B + b];
+    const int nlive = (L + p.chunk - 1) / p.chunk;
+    const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
+    const int64_t slot0 = (int64_t)unit * p.nchunks;
+    if (nlive >= 2) {
+      for (int g = wave; g < ng; g += 4) {
+        float M = neg_inf();
+        for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float S = 0.f;
+        for (int cc = lane; cc < nlive; cc += 64) {
+          const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
+          w[cc][g] = e;
+          S += e;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+        const float invS = 1.0f / S;
+        for (int cc = lane; cc < nlive; cc += 64) w[cc][g] *= invS;
+        if (lane == 0) {
+          const float l = M + logf(S);
+          p.lse_part[orow0 + g] = l;
+          s_lse[g] = l;
+        }
+      }
+    } else if (t < ng) {
+      s_lse[t] = p.lse_part[orow0 + t];  // written by the attention kernel (0 or 1 chunk)
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      if (k >= nrounds) break;  // uniform
+      const int e = k * per + t % per;
+      const int part_id = t / per;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      if (e < E) {
+        const int g = e / Q;
+        if (nlive >= 2) {
+          const float* src = p.ws_o + (slot0 * p.Gb + g) * D + 4 * (e % Q);
+          const int64_t cstride = (int64_t)p.Gb * D;
+#pragma unroll 4
+          for (int cc = part_id; cc < nlive; cc += P)
+            y += w[cc][g] * *reinterpret_cast<const f32x4*>(src + cc * cstride);
+        } else if (part_id == 0 && nlive == 1) {
+          y = load4(p.o_part, (orow0 + g) * D + 4 * (e % Q), p.odt);
+        }
+      }
+      if (P > 1 && nlive >= 2) {
+        part[t] = y;
+        __syncthreads();
+        if (part_id == 0 && e < E)
+          for (int q = 1; q < P; ++q) y += part[t + q * per];
+        __syncthreads();
+      }
+      if (part_id == 0 && e < E) {
+        const int g = e / Q;
+        if (nlive >= 2) store4(p.o_part, (orow0 + g) * D + 4 * (e % Q), y, p.odt);
+        const float l = s_lse[g];
+        if (l != neg_inf()) {  // online merge across shards, shard order
+          const float Mn = fmaxf(Mrun[k], l);
+          const double a = exp((double)Mrun[k] - (double)Mn);  // 0 while nothing merged
+          const double e2 = exp((double)l - (double)Mn);
+          Srun[k] = Srun[k] * a + e2;
+          acc[k] = acc[k] * (float)a + (float)e2 * y;
+          Mrun[k] = Mn;
+        }
+      }
+    }
+    __syncthreads();  // s_lse and w are rewritten for the next shard
+  }
+
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int e = k * per + t % per;
+    if (k >= nrounds || t / per != 0 || e >= E) continue;
+    const int g = e / Q;
+    const int64_t row = (int64_t)b * p.Hq + h * p.G + g0 + g;
+    if (Mrun[k] == neg_inf()) {
+      store4(out, row * D + 4 * (e % Q), f32x4{0.f, 0.f, 0.f, 0.f}, out_dt);
+      if (lse_out != nullptr && e % Q == 0) lse_out[row] = neg_inf();
+    } else {
+      store4(out, row * D + 4 * (e % Q), acc[k] * (float)(1.0 / Srun[k]), out_dt);
+      if (lse_out != nullptr && e % Q == 0) lse_out[row] = (float)((double)Mrun[k] + log(Srun[k]));
+    }
+  }
+}
+
 template <typename T, int D, int NW>
-hipError_t launch_typed(const AttnParams& p, int64_t units, hipStream_t s) {
+hipError_t launch_typed(const AttnParams& p, int64_t units, const StepOut* so, hipStream_t s) {
   const int64_t blocks = units * p.nchunks;
   hipLaunchKernelGGL((attn_partial_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, s,
                      p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nchunks < 2) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (so != nullptr && p.nchunks >= 2) {  // the whole step: chunk merge + shard merge fused
+    hipLaunchKernelGGL((attn_combine_merge_kernel<D>), dim3((unsigned)(units / p.R)), dim3(256), 0,
+                       s, p, so->out, so->lse_out, so->out_dt);
+    return hipGetLastError();
+  }
+  if (p.nchunks >= 2) {
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (so != nullptr)  // the whole step, unsplit: the cross-shard merge reads o_part
+    return launch_lse_merge(p.o_part, p.lse_part, p.R, (int64_t)p.B * p.Hq, D, p.odt, so->out_dt,
+                            so->out, so->lse_out, s);
+  return hipSuccess;
 }
 
 template <typename T, int D>
-hipError_t launch_w(const AttnParams& p, int waves, int64_t units, hipStream_t s) {
+hipError_t launch_w(const AttnParams& p, int waves, int64_t units, const StepOut* so,
+                    hipStream_t s) {
   switch (waves) {
-    case 1: return launch_typed<T, D, 1>(p, units, s);
-    case 2: return launch_typed<T, D, 2>(p, units, s);
-    case 4: return launch_typed<T, D, 4>(p, units, s);
-    case 8: return launch_typed<T, D, 8>(p, units, s);
+    case 1: return launch_typed<T, D, 1>(p, units, so, s);
+    case 2: return launch_typed<T, D, 2>(p, units, so, s);
+    case 4: return launch_typed<T, D, 4>(p, units, so, s);
+    case 8: return launch_typed<T, D, 8>(p, units, so, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_d(const AttnParams& p, int D, int waves, int64_t units, hipStream_t s) {
+hipError_t launch_d(const AttnParams& p, int D, int waves, int64_t units, const StepOut* so,
+                    hipStream_t s) {
   switch (D) {
-    case 64: return launch_w<T, 64>(p, waves, units, s);
-    case 128: return launch_w<T, 128>(p, waves, units, s);
-    case 256: return launch_w<T, 256>(p, waves, units, s);
+    case 64: return launch_w<T, 64>(p, waves, units, so, s);
+    case 128: return launch_w<T, 128>(p, waves, units, so, s);
+    case 256: return launch_w<T, 256>(p, waves, units, so, s);
   }
   return hipErrorInvalidValue;
 }
@@ -465,9 +620,9 @@ __global__ void clear_tail_kernel(unsigned char* q, size_t n) {
 }  // namespace
 
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves, int64_t units,
-                               hipStream_t s) {
-  if (qkv_dt == kBF16) return launch_d<bf16_t>(p, D, waves, units, s);
-  if (qkv_dt == kF16) return launch_d<f16_t>(p, D, waves, units, s);
+                               const StepOut* so, hipStream_t s) {
+  if (qkv_dt == kBF16) return launch_d<bf16_t>(p, D, waves, units, so, s);
+  if (qkv_dt == kF16) return launch_d<f16_t>(p, D, waves, units, so, s);
   return hipErrorInvalidValue;
 }
 

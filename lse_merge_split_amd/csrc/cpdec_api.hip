@@ -141,10 +141,37 @@ cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens, in
   return CPDEC_OK;
 }
 
+static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
+                                const void* const* k_shards, const void* const* v_shards,
+                                const int32_t* lens, void* o_part, float* lse_part,
+                                void* workspace, size_t workspace_bytes, const StepOut* so,
+                                void* stream);
+
 cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
                                 const void* const* k_shards, const void* const* v_shards,
                                 const int32_t* lens, void* o_part, float* lse_part,
                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_launch(d, q, k_shards, v_shards, lens, o_part, lse_part, workspace,
+                     workspace_bytes, nullptr, stream);
+}
+
+cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
+                             const void* const* k_shards, const void* const* v_shards,
+                             const int32_t* lens, void* o_part, float* lse_part, void* out,
+                             float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (out == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return CPDEC_ERR_ALIGNMENT;
+  StepOut so{out, lse_out, d != nullptr ? (int)d->qkv_dtype : 0};
+  return attn_launch(d, q, k_shards, v_shards, lens, o_part, lse_part, workspace,
+                     workspace_bytes, &so, stream);
+}
+
+static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
+                                const void* const* k_shards, const void* const* v_shards,
+                                const int32_t* lens, void* o_part, float* lse_part,
+                                void* workspace, size_t workspace_bytes, const StepOut* so,
+                                void* stream) {
   AttnPlan pl;
   cpdec_status st = plan_attn(d, &pl);
   if (st != CPDEC_OK) return st;
@@ -196,7 +223,7 @@ cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
   const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
 
-  hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units,
+  hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units, so,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CPDEC_OK : CPDEC_ERR_HIP;
 }

@@ -28,10 +28,19 @@ struct AttnParams {
   float scale_log2;   // sm_scale * log2(e)
 };
 
+// Where the whole step (cpdec_cp_decode) writes the merged result.
+struct StepOut {
+  void* out;
+  float* lse_out;  // may be null
+  int out_dt;
+};
+
 // Launch the partial-attention kernel over units x nchunks workgroups, then
 // (when a unit can span several chunks) the chunk-combine kernel over units.
+// With `so` the cross-shard merge follows: fused into the chunk merge when
+// shards are split, else the plain merge kernel (two launches either way).
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
-                               int64_t units, hipStream_t s);
+                               int64_t units, const StepOut* so, hipStream_t s);
 
 hipError_t launch_lse_merge(const void* o, const float* lse, int R, int64_t rows, int D,
                             int in_dt, int out_dt, void* out, float* lse_out, hipStream_t s);

@@ -123,6 +123,20 @@ def test_attn_pointer_errors():
 
 
 @needs_cpu_host
+def test_cp_decode_errors():
+    d = _desc(chunk_tokens=1024)
+    f = cp.lib().cpdec_cp_decode
+    ks = (ctypes.c_void_p * 4)(*([A] * 4))
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, None, A, None, 0, None) == INVALID
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A + 8, A, None, 0, None) == ALIGN
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A + 2, None, 0, None) == ALIGN
+    bad = _desc(chunk_tokens=1024, head_dim=96)
+    assert f(ctypes.byref(bad), A, ks, ks, A, A, A, A, A, None, 0, None) == UNSUPPORTED
+    split = _desc(chunk_tokens=128)
+    assert f(ctypes.byref(split), A, ks, ks, A, A, A, A, A, None, 0, None) == WS
+
+
+@needs_cpu_host
 def test_merge_errors():
     m = cp.lib().cpdec_lse_merge
     assert m(None, A, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
