@@ -177,11 +177,12 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  * o_part/lse_part exactly as that call writes them) and their LSE merge into
  * out/lse_out, with the merge formula of cpdec_lse_merge (page sections
  * "Introduction" and "Code analysis, 1. Fused kernel").  When shards are split
- * into chunks the per-shard chunk merge and the cross-shard merge share one
- * kernel (one launch fewer than the two calls); otherwise the second launch is
- * cpdec_lse_merge itself.  The cross-shard sum runs as an online merge in
- * shard order, so `out` agrees with cpdec_lse_merge of the same partials to
- * rounding, not bit for bit, in the split case.
+ * into chunks (and the per-shard state of a (sequence, kv head) fits the
+ * kernel's on-chip buffers: shards x chunks <= 512, shards x heads x D/4 <=
+ * 1024) the per-shard chunk merge and the cross-shard merge share one kernel
+ * (one launch fewer than the two calls); otherwise the chunk merge and
+ * cpdec_lse_merge's kernel run as separate launches.  `out` agrees with
+ * cpdec_lse_merge of the same partials to rounding.
  *
  *   d, q, k_shards, v_shards, lens, o_part, lse_part, workspace,
  *   workspace_bytes, stream   as for cpdec_attn_partial

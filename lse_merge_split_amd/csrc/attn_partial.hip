@@ -428,18 +428,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
 }
 
-// The whole step's second launch: for one (sequence, kv head, head block)
-// merge each shard's chunk partials into o_part/lse_part (as
-// attn_combine_kernel does; shards that fit one chunk were written by the
-// attention kernel and are read back), then merge the shards into out/lse_out
-// with an online LSE merge in shard order (FP64 weight sum, FP32 output
-// sum; -inf shards are skipped, so they cannot leak).
+// The whole step's second launch, for one (sequence, kv head, head block)
+// and all R shards at once: (1) per (shard, head) the chunk weights (wave
+// reductions), (2) per (shard, output vector) the shard's partial -- merged
+// from its chunks and written to o_part, or read back when the attention
+// kernel wrote it (0 or 1 live chunk) -- kept in LDS, (3) the cross-shard
+// merge in shard order (FP64 weights and lse, FP32 sums, -inf shards
+// skipped) into out/lse_out.  Used when the per-shard state fits LDS
+// (kFusedChunkSlots, kFusedVecs); otherwise the separate kernels run.
+constexpr int kFusedChunkSlots = 512;  // R * chunks
+constexpr int kFusedVecs = 1024;       // R * (heads * D / 4)
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_merge_kernel(const AttnParams p, void* out,
                                                                  float* lse_out, int out_dt) {
-  __shared__ float w[kMaxChunks][16];
+  __shared__ float w[kFusedChunkSlots][16];
+  __shared__ f32x4 ybuf[kFusedVecs];
   __shared__ f32x4 part[256];
-  __shared__ float s_lse[16];
+  __shared__ float s_lse[kMaxShards][16];
+  __shared__ int s_nlive[kMaxShards];
   const int bh = blockIdx.x;  // ((b * Hkv) + h) * gblocks + gb
   const int gb = bh % p.gblocks;
   const int h = (bh / p.gblocks) % p.Hkv;
@@ -449,115 +456,111 @@ __global__ __launch_bounds__(256) void attn_combine_merge_kernel(const AttnParam
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int t = threadIdx.x;
+  const int R = p.R;
+  auto unit_of = [&](int r) { return ((r * p.B + b) * p.Hkv + h) * p.gblocks + gb; };
+  auto orow_of = [&](int r) { return ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0; };
 
+  if (t < R) {
+    const int L = p.lens[t * p.B + b];
+    s_nlive[t] = (L + p.chunk - 1) / p.chunk;
+  }
+  __syncthreads();
+
+  // (1) chunk weights and shard lse, one (shard, head) pair per wave in turn
+  for (int pi = wave; pi < R * ng; pi += 4) {
+    const int r = pi / ng, g = pi % ng;
+    const int nlive = s_nlive[r];
+    if (nlive < 2) {  // 0 or 1 live chunk: the attention kernel wrote lse_part
+      if (lane == 0) s_lse[r][g] = p.lse_part[orow_of(r) + g];
+      continue;
+    }
+    const int64_t slot0 = (int64_t)unit_of(r) * p.nchunks;
+    float M = neg_inf();
+    for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float S = 0.f;
+    for (int cc = lane; cc < nlive; cc += 64) {
+      const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
+      w[r * p.nchunks + cc][g] = e;
+      S += e;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+    const float invS = 1.0f / S;
+    for (int cc = lane; cc < nlive; cc += 64) w[r * p.nchunks + cc][g] *= invS;
+    if (lane == 0) {
+      const float l = M + logf(S);
+      p.lse_part[orow_of(r) + g] = l;
+      s_lse[r][g] = l;
+    }
+  }
+  __syncthreads();
+
+  // (2) every shard's partial vectors (chunks split over P thread groups)
   constexpr int Q = D / 4;               // float4 outputs per head
-  const int E = ng * Q;                  // float4 outputs of this head block
-  int P = 1;                             // chunk partitions
-  while (P < 8 && E * P * 2 <= 256) P *= 2;
+  const int E = ng * Q;                  // float4 outputs per shard
+  const int items = R * E;
+  int P = 1;
+  while (P < 8 && items * P * 2 <= 256) P *= 2;
   const int per = 256 / P;
-  constexpr int kRounds = (kGroupRows * (D / 4) + 255) / 256;  // element rounds per thread (<= 4)
-  const int nrounds = (E + per - 1) / per;
-
-  // running cross-shard state per owned element (partition 0 only): head max,
-  // FP64 weight sum and FP32 output sum
-  float Mrun[kRounds];
-  double Srun[kRounds];
-  f32x4 acc[kRounds];
-#pragma unroll
-  for (int k = 0; k < kRounds; ++k) {
-    Mrun[k] = neg_inf();
-    Srun[k] = 0.0;
-    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int r = 0; r < p.R; ++r) {
-    const int unit = ((r * p.B + b) * p.Hkv + h) * p.gblocks + gb;
-    const int L = p.lens[r * p.B + b];
-    const int nlive = (L + p.chunk - 1) / p.chunk;
-    const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
-    const int64_t slot0 = (int64_t)unit * p.nchunks;
-    if (nlive >= 2) {
-      for (int g = wave; g < ng; g += 4) {
-        float M = neg_inf();
-        for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        float S = 0.f;
-        for (int cc = lane; cc < nlive; cc += 64) {
-          const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
-          w[cc][g] = e;
-          S += e;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-        const float invS = 1.0f / S;
-        for (int cc = lane; cc < nlive; cc += 64) w[cc][g] *= invS;
-        if (lane == 0) {
-          const float l = M + logf(S);
-          p.lse_part[orow0 + g] = l;
-          s_lse[g] = l;
-        }
-      }
-    } else if (t < ng) {
-      s_lse[t] = p.lse_part[orow0 + t];  // written by the attention kernel (0 or 1 chunk)
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int k = 0; k < kRounds; ++k) {
-      if (k >= nrounds) break;  // uniform
-      const int e = k * per + t % per;
-      const int part_id = t / per;
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      if (e < E) {
-        const int g = e / Q;
-        if (nlive >= 2) {
-          const float* src = p.ws_o + (slot0 * p.Gb + g) * D + 4 * (e % Q);
-          const int64_t cstride = (int64_t)p.Gb * D;
+  const int part_id = t / per;
+  for (int i0 = 0; i0 < items; i0 += per) {
+    const int it = i0 + t % per;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    int r = 0, e = 0, nlive = 0;
+    if (it < items) {
+      r = it / E;
+      e = it % E;
+      nlive = s_nlive[r];
+      const int g = e / Q;
+      if (nlive >= 2) {
+        const int64_t slot0 = (int64_t)unit_of(r) * p.nchunks;
+        const float* src = p.ws_o + (slot0 * p.Gb + g) * D + 4 * (e % Q);
+        const int64_t cstride = (int64_t)p.Gb * D;
 #pragma unroll 4
-          for (int cc = part_id; cc < nlive; cc += P)
-            y += w[cc][g] * *reinterpret_cast<const f32x4*>(src + cc * cstride);
-        } else if (part_id == 0 && nlive == 1) {
-          y = load4(p.o_part, (orow0 + g) * D + 4 * (e % Q), p.odt);
-        }
-      }
-      if (P > 1 && nlive >= 2) {
-        part[t] = y;
-        __syncthreads();
-        if (part_id == 0 && e < E)
-          for (int q = 1; q < P; ++q) y += part[t + q * per];
-        __syncthreads();
-      }
-      if (part_id == 0 && e < E) {
-        const int g = e / Q;
-        if (nlive >= 2) store4(p.o_part, (orow0 + g) * D + 4 * (e % Q), y, p.odt);
-        const float l = s_lse[g];
-        if (l != neg_inf()) {  // online merge across shards, shard order
-          const float Mn = fmaxf(Mrun[k], l);
-          const double a = exp((double)Mrun[k] - (double)Mn);  // 0 while nothing merged
-          const double e2 = exp((double)l - (double)Mn);
-          Srun[k] = Srun[k] * a + e2;
-          acc[k] = acc[k] * (float)a + (float)e2 * y;
-          Mrun[k] = Mn;
-        }
+        for (int cc = part_id; cc < nlive; cc += P)
+          y += w[r * p.nchunks + cc][g] * *reinterpret_cast<const f32x4*>(src + cc * cstride);
+      } else if (nlive == 1 && part_id == 0) {
+        y = load4(p.o_part, (orow_of(r) + g) * D + 4 * (e % Q), p.odt);
       }
     }
-    __syncthreads();  // s_lse and w are rewritten for the next shard
+    if (P > 1) {
+      part[t] = y;
+      __syncthreads();
+      if (part_id == 0 && it < items)
+        for (int q = 1; q < P; ++q) y += part[t + q * per];
+      __syncthreads();
+    }
+    if (part_id == 0 && it < items) {
+      if (nlive >= 2) store4(p.o_part, (orow_of(r) + e / Q) * D + 4 * (e % Q), y, p.odt);
+      ybuf[it] = y;
+    }
   }
+  __syncthreads();
 
-#pragma unroll
-  for (int k = 0; k < kRounds; ++k) {
-    const int e = k * per + t % per;
-    if (k >= nrounds || t / per != 0 || e >= E) continue;
+  // (3) cross-shard merge in shard order
+  for (int e = t; e < E; e += 256) {
     const int g = e / Q;
+    float M = neg_inf();
+    for (int r = 0; r < R; ++r) M = fmaxf(M, s_lse[r][g]);
     const int64_t row = (int64_t)b * p.Hq + h * p.G + g0 + g;
-    if (Mrun[k] == neg_inf()) {
+    if (M == neg_inf()) {
       store4(out, row * D + 4 * (e % Q), f32x4{0.f, 0.f, 0.f, 0.f}, out_dt);
       if (lse_out != nullptr && e % Q == 0) lse_out[row] = neg_inf();
-    } else {
-      store4(out, row * D + 4 * (e % Q), acc[k] * (float)(1.0 / Srun[k]), out_dt);
-      if (lse_out != nullptr && e % Q == 0) lse_out[row] = (float)((double)Mrun[k] + log(Srun[k]));
+      continue;
     }
+    double S = 0.0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r) {
+      const float l = s_lse[r][g];
+      if (l == neg_inf()) continue;  // empty shard: never used
+      const double ew = exp((double)l - (double)M);
+      S += ew;
+      acc += (float)ew * ybuf[r * E + e];
+    }
+    store4(out, row * D + 4 * (e % Q), acc * (float)(1.0 / S), out_dt);
+    if (lse_out != nullptr && e % Q == 0) lse_out[row] = (float)((double)M + log(S));
   }
 }
 
@@ -568,7 +571,9 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, const StepOut* so, h
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (so != nullptr && p.nchunks >= 2) {  // the whole step: chunk merge + shard merge fused
+  const int64_t fused_vecs = (int64_t)p.R * p.Gb * (D / 4);
+  if (so != nullptr && p.nchunks >= 2 && (int64_t)p.R * p.nchunks <= kFusedChunkSlots &&
+      fused_vecs <= kFusedVecs) {  // the whole step: chunk merge + shard merge fused
     hipLaunchKernelGGL((attn_combine_merge_kernel<D>), dim3((unsigned)(units / p.R)), dim3(256), 0,
                        s, p, so->out, so->lse_out, so->out_dt);
     return hipGetLastError();

@@ -47,12 +47,15 @@ def test_step_matches_oracle_and_two_calls(name):
     inp = sg.attn_inputs(w)
     step = run_step(inp)
     two = run_path(inp)
-    # the partials are the same kernels' output
-    assert torch.equal(step["o_part"], two["o_part"]) and torch.equal(step["lse_part"], two["lse_part"])
+    # same per-shard statistics; the chunk sums may be split over a different
+    # number of thread groups, so o_part agrees to FP32 rounding
+    assert torch.equal(step["lse_part"], two["lse_part"])
+    assert torch.allclose(step["o_part"], two["o_part"], rtol=1e-5, atol=1e-6)
     for b in range(w.B):
         for h in range(w.Hkv):
             ref = ow.group(w, inp["lens_np"], b, h)
             hs = slice(h * w.G, (h + 1) * w.G)
+            assert_out(to64(step["o_part"][:, b, hs]), ref["o_part"], f"o_part b={b} h={h}")
             assert_out(to64(step["out"][b, hs]), ref["out"], f"out b={b} h={h}")
             assert_lse(to64(step["lse_out"][b, hs]), ref["lse_out"], f"lse_out b={b} h={h}")
 
