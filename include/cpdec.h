@@ -86,8 +86,28 @@ typedef struct cpdec_attn_desc {
  * Bytes of device workspace cpdec_attn_partial needs for `d` (0 when every
  * shard fits one chunk).  Returns 0 for an invalid descriptor as well; such a
  * descriptor is then rejected by cpdec_attn_partial itself.
+ *
+ * Workspace layout, shared by both attention entry points: the first
+ * CPDEC_STEP_COUNTER_BYTES bytes hold cpdec_cp_decode's arrival counters and
+ * are never written by cpdec_attn_partial; the chunk partials follow.
  */
+#define CPDEC_STEP_COUNTER_BYTES 65536
 size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
+
+/*
+ * Bytes of device workspace cpdec_cp_decode needs for `d`: the counter region
+ * plus the chunk partials, so always at least CPDEC_STEP_COUNTER_BYTES (0 for
+ * an invalid descriptor).  A workspace of this size also serves
+ * cpdec_attn_partial for the same descriptor.
+ */
+size_t cpdec_step_workspace_bytes(const cpdec_attn_desc* d);
+
+/*
+ * Number of kernel launches cpdec_cp_decode makes for `d`: 1 (the usual case),
+ * or 2/3 when a limit of the one-launch form is exceeded (see
+ * cpdec_cp_decode).  Errors: the descriptor checks of cpdec_attn_partial.
+ */
+cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches);
 
 /*
  * The launch plan cpdec_attn_partial uses for `d`: the split-KV chunk length
@@ -125,7 +145,8 @@ cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens,
  *                256-byte aligned; may be NULL when that size is 0.  Scratch
  *                for the split-KV chunk partials; its contents on entry do not
  *                matter (no clearing is needed, also when one buffer serves
- *                descriptors of different shapes).  When that size is non-zero
+ *                descriptors of different shapes), and the counter region at
+ *                its start is left untouched.  When that size is non-zero
  *                the call enqueues two kernels (attention, then the merge of
  *                each shard's chunk partials), otherwise one.
  *   stream       hipStream_t
@@ -173,23 +194,33 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
                              void* out, float* lse_out, void* stream);
 
 /*
- * The whole step in two launches: cpdec_attn_partial's partials (written to
- * o_part/lse_part exactly as that call writes them) and their LSE merge into
- * out/lse_out, with the merge formula of cpdec_lse_merge (page sections
- * "Introduction" and "Code analysis, 1. Fused kernel").  When shards are split
- * into chunks (and the per-shard state of a (sequence, kv head) fits the
- * kernel's on-chip buffers: shards x chunks <= 512, shards x heads x D/4 <=
- * 1024) the per-shard chunk merge and the cross-shard merge share one kernel
- * (one launch fewer than the two calls); otherwise the chunk merge and
- * cpdec_lse_merge's kernel run as separate launches.  `out` agrees with
- * cpdec_lse_merge of the same partials to rounding.
+ * The whole step: cpdec_attn_partial's partials (o_part/lse_part, same
+ * values to FP32 rounding) and their LSE merge into out/lse_out with the merge
+ * formula of cpdec_lse_merge (page sections "Introduction" and "Code
+ * analysis, 1. Fused kernel"), normally in ONE kernel launch: every
+ * workgroup hands its partial over through device-scope stores and an
+ * arrival counter per (sequence, kv head); the last workgroup of each such
+ * group combines its shards' chunks, writes o_part/lse_part and merges the
+ * shards.  The result does not depend on which workgroup arrives last.
+ * Limits of the one-launch form: (sequences x kv heads x ceil(G/16)) <= 16384,
+ * o_part below 2 GiB and, when shards are split into chunks, shards x chunks x
+ * min(G,16) <= 2048 and shards x min(G,16) x D/4 <= 2048; beyond them the
+ * step runs as attention, chunk-merge and merge launches (cpdec_step_plan
+ * tells which).  `out` agrees with cpdec_lse_merge of the same partials to
+ * rounding.
  *
- *   d, q, k_shards, v_shards, lens, o_part, lse_part, workspace,
- *   workspace_bytes, stream   as for cpdec_attn_partial
+ *   d, q, k_shards, v_shards, lens, o_part, lse_part, stream
+ *              as for cpdec_attn_partial
  *   out        device, [B][Hq][D] in qkv_dtype, 16-byte aligned
  *   lse_out    device, float [B][Hq], or NULL to skip writing it
+ *   workspace  device, at least cpdec_step_workspace_bytes(d) bytes, 256-byte
+ *              aligned.  Its first CPDEC_STEP_COUNTER_BYTES bytes must be zero
+ *              before the first call on it (cpdec_workspace_clear does that
+ *              once, after allocation); every call that completes leaves them
+ *              zero again, whatever the shape.  The rest is scratch.  Two calls
+ *              that may run at the same time need separate workspaces.
  * Errors: as cpdec_attn_partial; INVALID_ARG for a NULL out; ALIGNMENT for a
- * misaligned out or lse_out.
+ * misaligned out or lse_out; WORKSPACE for a missing or short workspace.
  */
 cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
                              const void* const* k_shards,
@@ -200,9 +231,10 @@ cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
 
 /*
  * Zero-fill `bytes` bytes of a buffer on `stream` with a kernel (no
- * hipMemset, so it is safe to record in a HIP graph).  Workspaces do not need
- * it; it is offered for callers that want deterministic buffer contents.
- * `workspace` must be 256-byte aligned.  Errors: INVALID_ARG, ALIGNMENT, HIP.
+ * hipMemset, so it is safe to record in a HIP graph).  A new workspace for
+ * cpdec_cp_decode needs it once (its counter region must start at zero);
+ * cpdec_attn_partial needs no clearing.  `workspace` must be 256-byte
+ * aligned.  Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 cpdec_status cpdec_workspace_clear(void* workspace, size_t bytes, void* stream);
 

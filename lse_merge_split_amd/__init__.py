@@ -15,8 +15,9 @@ import ctypes
 import os
 
 __all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "StepCall", "attn_partial",
-           "lse_merge", "cp_decode",
-           "attn_workspace_bytes", "attn_plan", "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS"]
+           "lse_merge", "cp_decode", "attn_workspace_bytes", "step_workspace_bytes", "attn_plan",
+           "step_launches", "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS",
+           "STEP_COUNTER_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpdec.so")
@@ -24,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libcpdec.so")
 STATUS = {0: "CPDEC_OK", 1: "CPDEC_ERR_INVALID_ARG", 2: "CPDEC_ERR_UNSUPPORTED",
           3: "CPDEC_ERR_ALIGNMENT", 4: "CPDEC_ERR_WORKSPACE", 5: "CPDEC_ERR_HIP"}
 F32, F16, BF16 = 0, 1, 2
+STEP_COUNTER_BYTES = 65536  # CPDEC_STEP_COUNTER_BYTES: counter region at the workspace start
 
 
 class CpdecError(RuntimeError):
@@ -56,7 +58,11 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.cpdec_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
         L.cpdec_attn_workspace_bytes.restype = sz
+        L.cpdec_step_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
+        L.cpdec_step_workspace_bytes.restype = sz
         pi = ctypes.POINTER(ctypes.c_int32)
+        L.cpdec_step_plan.argtypes = [ctypes.POINTER(AttnDesc), pi]
+        L.cpdec_step_plan.restype = ctypes.c_int
         L.cpdec_attn_plan.argtypes = [ctypes.POINTER(AttnDesc), pi, pi, pi]
         L.cpdec_attn_plan.restype = ctypes.c_int
         L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
@@ -129,20 +135,37 @@ def attn_plan(desc: AttnDesc) -> dict:
 
 
 def attn_workspace_bytes(desc: AttnDesc) -> int:
+    """Workspace bytes cpdec_attn_partial needs (0: none)."""
     return int(lib().cpdec_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def step_workspace_bytes(desc: AttnDesc) -> int:
+    """Workspace bytes cpdec_cp_decode needs (counter region + partials)."""
+    return int(lib().cpdec_step_workspace_bytes(ctypes.byref(desc)))
+
+
+def step_launches(desc: AttnDesc) -> int:
+    """Kernel launches cpdec_cp_decode makes for a descriptor (1 normally)."""
+    n = ctypes.c_int32()
+    rc = lib().cpdec_step_plan(ctypes.byref(desc), ctypes.byref(n))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_step_plan")
+    return n.value
 
 
 _WS_CACHE: dict = {}
 
 
 def _workspace(device, nbytes):
-    """A workspace of at least nbytes, reused across calls and shapes (the
-    library needs no particular contents on entry)."""
+    """A workspace of at least nbytes, reused across calls and shapes.  It is
+    zero-filled when allocated: cpdec_cp_decode needs its counter region to
+    start at zero, and every call leaves it zero (cpdec_attn_partial never
+    writes it)."""
     torch = _torch()
     key = (str(device),)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS_CACHE[key] = ws
     return ws
 
@@ -151,6 +174,8 @@ class AttnCall:
     """A cpdec_attn_partial call with its arguments marshalled once.
 
     Calling it enqueues the kernel on the current stream (or ``stream``)."""
+
+    _workspace_query = staticmethod(attn_workspace_bytes)
 
     def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
                  kv_capacity=None, workspace=None, chunk_tokens=0):
@@ -173,7 +198,7 @@ class AttnCall:
         if (tuple(lse_part.shape) != (R, desc.batch, desc.num_q_heads)
                 or tuple(lens.shape) != (R, desc.batch)):
             raise ValueError("lse_part must be [R, B, Hq] and lens [R, B]")
-        self.workspace_bytes = attn_workspace_bytes(desc)
+        self.workspace_bytes = self._workspace_query(desc)
         self.plan = attn_plan(desc)
         if workspace is None and self.workspace_bytes > 0:
             workspace = _workspace(q.device, self.workspace_bytes)
@@ -199,11 +224,16 @@ class AttnCall:
 
 
 class StepCall(AttnCall):
-    """A cpdec_cp_decode call (the whole step: partials and their merge, two
-    launches) with its arguments marshalled once."""
+    """A cpdec_cp_decode call (the whole step: partials and their merge,
+    normally one launch) with its arguments marshalled once.  A workspace
+    passed in must have its first STEP_COUNTER_BYTES bytes zero before the
+    first call (see workspace_clear)."""
+
+    _workspace_query = staticmethod(step_workspace_bytes)
 
     def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, **kw):
         super().__init__(q, k_shards, v_shards, lens, o_part, lse_part, **kw)
+        self.launches = step_launches(self.desc)
         if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
             raise ValueError("out must be a contiguous [B, Hq, D] tensor of q's dtype")
         if lse_out is not None and (tuple(lse_out.shape) != tuple(q.shape[:2])

@@ -15,12 +15,19 @@
 //   un-normalised accumulator) per query head, loading tile i+1 while it
 //   computes tile i.  The waves' states are merged through LDS.  A unit whose
 //   tokens fit one chunk is written straight to o_part/lse_part; otherwise each
-//   chunk writes a normalised partial to the workspace and a second, small
-//   kernel merges the chunks of every unit -- both merges use the same LSE
-//   weighting as the cross-shard merge, which the page's merge formula makes
-//   exact.  No workgroup waits on another inside a kernel: on gfx950 a
-//   device-scope release/acquire pair writes back and invalidates the L2 of
-//   the XCD, which costs more than a second launch.
+//   chunk writes a normalised partial to the workspace.  Every merge -- chunks
+//   of a shard, shards of a sequence -- uses the LSE weighting of the page's
+//   merge formula, which makes it exact.
+//
+// Who merges:
+//   * partials only (cpdec_attn_partial): a second, small kernel merges the
+//     chunks of every unit.
+//   * the whole step in one launch (cpdec_cp_decode): workgroups hand their
+//     results over with device-scope stores and an arrival counter per
+//     (sequence, kv head, head block); the workgroup that arrives last merges
+//     that group's chunks and shards.  No workgroup ever waits for another,
+//     and no device-scope fence is used: on gfx950 such a fence writes back
+//     and invalidates the XCD's L2, which costs microseconds per workgroup.
 //
 // Per 32-token tile, with G <= 16 query heads of one kv head as MFMA columns:
 //   S^T[t][g] = K[t][:] . Q[g][:]       4 (D/32) MFMA 16x16x32 per 16 tokens;
@@ -106,44 +113,163 @@ struct Smem {
   float l[NW][16];
 };
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams p) {
+// LDS of the workgroup that merges a group in a one-launch step (shares the
+// attention's LDS: it is used only after the workgroup's own chunk is done).
+template <int NW, int MODE>
+struct MergeSmem {
+  static constexpr bool kChunks = MODE == kStepOneChunks;
+  float w[kChunks ? kStepSlots : 1];    // chunk weights, [(r * ng + g) * nchunks + c]
+  f32x4 y[kChunks ? kStepVecs : 1];     // shard partials as stored, [r * E + e]
+  f32x4 part[kChunks ? NW * 64 : 1];    // partition sums
+  float lse[kMaxShards * kGroupRows];   // shard lse, [r * ng + g]
+  double ew[kMaxShards * kGroupRows];   // cross-shard weights e^(lse - M), [r * ng + g]
+  float M[kGroupRows];                  // max shard lse per head
+};
+
+template <typename T, int D, int NW, int MODE>
+union KernelSmem {
+  Smem<D, NW> a;
+  MergeSmem<NW, MODE> m;
+};
+
+// 32 consecutive fp32 values, converted to dtype `odt`, written with
+// device-scope stores at byte offset `off` of resource `r`.
+__device__ __forceinline__ void store32_dev(rsrc_t r, uint32_t off, const float* x, int odt) {
+  if (odt == kF32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st16_dev(r, off + 16u * i,
+               __builtin_bit_cast(u32x4, f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]}));
+  } else if (odt == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st16_dev(r, off + 16u * i,
+               u32x4{pack2<bf16_t>(x[8 * i], x[8 * i + 1]), pack2<bf16_t>(x[8 * i + 2], x[8 * i + 3]),
+                     pack2<bf16_t>(x[8 * i + 4], x[8 * i + 5]), pack2<bf16_t>(x[8 * i + 6], x[8 * i + 7])});
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st16_dev(r, off + 16u * i,
+               u32x4{pack2<f16_t>(x[8 * i], x[8 * i + 1]), pack2<f16_t>(x[8 * i + 2], x[8 * i + 3]),
+                     pack2<f16_t>(x[8 * i + 4], x[8 * i + 5]), pack2<f16_t>(x[8 * i + 6], x[8 * i + 7])});
+  }
+}
+
+// 4 consecutive values of dtype `odt` at byte offset `off`, device-scope load.
+__device__ __forceinline__ f32x4 load4_dev(rsrc_t r, uint32_t off, int odt) {
+  if (odt == kF32) return __builtin_bit_cast(f32x4, ld16_dev(r, off));
+  const u32x2 w = ld8_dev(r, off);
+  if (odt == kBF16) return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+  return f32x4{f16_lo(w[0]), f16_hi(w[0]), f16_lo(w[1]), f16_hi(w[1])};
+}
+
+// The values x takes once stored as dtype `odt`.
+__device__ __forceinline__ f32x4 round4(f32x4 x, int odt) {
+  if (odt == kBF16) {
+    const uint32_t a = pack2<bf16_t>(x[0], x[1]), b = pack2<bf16_t>(x[2], x[3]);
+    return f32x4{bf16_lo(a), bf16_hi(a), bf16_lo(b), bf16_hi(b)};
+  }
+  if (odt == kF16) {
+    const uint32_t a = pack2<f16_t>(x[0], x[1]), b = pack2<f16_t>(x[2], x[3]);
+    return f32x4{f16_lo(a), f16_hi(a), f16_lo(b), f16_hi(b)};
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t esize(int dt) { return dt == kF32 ? 4u : 2u; }
+
+// Scalar launch parameters, read once at kernel start.  Each value passes
+// through an empty asm statement that makes it opaque to the compiler, so it
+// stays in a register (or a VGPR lane when registers run short) instead of
+// being fetched again from the kernel arguments later: the argument buffer is
+// not cached, and each such re-fetch would cost a memory round trip in the
+// latency-bound tail of a workgroup (its stores, the arrival, the merge).
+struct Args {
+  const void* q;
+  const int32_t* lens;
+  void* o_part;
+  float* lse_part;
+  float* ws_o;
+  float* ws_lse;
+  void* out;
+  float* lse_out;
+  int32_t* counters;
+  int64_t sb, sh, st;
+  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt, out_dt;
+  float scale_log2;
+};
+
+// (readfirstlane afterwards: the compiler takes an asm result for a per-lane
+// value, and a buffer resource built from one would need a waterfall loop.)
+__device__ __forceinline__ uint32_t opaque32(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+template <typename V>
+__device__ __forceinline__ V opaque(V x) {
+  static_assert(sizeof(V) == 4 || sizeof(V) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(V) == 4) {
+    return __builtin_bit_cast(V, opaque32(__builtin_bit_cast(uint32_t, x)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint64_t lo = opaque32((uint32_t)u), hi = opaque32((uint32_t)(u >> 32));
+    return __builtin_bit_cast(V, lo | (hi << 32));
+  }
+}
+
+__device__ __forceinline__ Args load_args(const AttnParams& p) {
+  Args a;
+  a.q = opaque(p.q);
+  a.lens = opaque(p.lens);
+  a.o_part = opaque(p.o_part);
+  a.lse_part = opaque(p.lse_part);
+  a.ws_o = opaque(p.ws_o);
+  a.ws_lse = opaque(p.ws_lse);
+  a.out = opaque(p.out);
+  a.lse_out = opaque(p.lse_out);
+  a.counters = opaque(p.counters);
+  a.sb = opaque(p.sb);
+  a.sh = opaque(p.sh);
+  a.st = opaque(p.st);
+  a.B = opaque(p.B);
+  a.Hq = opaque(p.Hq);
+  a.Hkv = opaque(p.Hkv);
+  a.G = opaque(p.G);
+  a.Gb = opaque(p.Gb);
+  a.gblocks = opaque(p.gblocks);
+  a.R = opaque(p.R);
+  a.chunk = opaque(p.chunk);
+  a.nchunks = opaque(p.nchunks);
+  a.units = opaque(p.units);
+  a.odt = opaque(p.odt);
+  a.out_dt = opaque(p.out_dt);
+  a.scale_log2 = opaque(p.scale_log2);
+  return a;
+}
+
+// Attention of one workgroup over chunk c of `unit` (t_begin < L): the
+// normalised chunk result goes to o_part/lse_part when the unit has one live
+// chunk, else to the workspace.  In the one-launch step modes these stores are
+// device-scope, for the workgroup that merges the group.
+template <typename T, int D, int NW, int MODE>
+__device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, const void* vshard,
+                                             Smem<D, NW>& sm, int c, int unit, int r, int b, int h,
+                                             int gb, int L) {
   constexpr int NCH = D / 8;           // 16-byte chunks per token row
   constexpr int NB = (NCH + 15) / 16;  // 16-chunk row blocks of the PV product
   constexpr int KS = D / 32;           // k-steps of the QK product
-  __shared__ Smem<D, NW> sm;
+  constexpr bool kDev = MODE >= kStepOneShards;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // Chunk-major order: workgroups are dealt to the 8 XCDs round-robin by
-  // block index, so block % 8 must not correlate with the chunk index (the
-  // later chunks of ragged shards are mostly empty); here it follows the unit.
-  const int c = blockIdx.x / p.units;
-  const int unit = blockIdx.x % p.units;
-  int u = unit;
-  const int gb = u % p.gblocks; u /= p.gblocks;
-  const int h = u % p.Hkv; u /= p.Hkv;
-  const int b = u % p.B;
-  const int r = u / p.B;
-
-  const int L = p.lens[r * p.B + b];
   const int t_begin = c * p.chunk;
   const int g0 = gb * kGroupRows;
   const int ng = min(kGroupRows, p.G - g0);
   const int hq0 = h * p.G + g0;
   const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + hq0;  // o_part/lse_part row of head g0
-
-  if (t_begin >= L) {
-    if (c == 0) {  // empty shard: o_r = 0, lse_r = -inf
-      for (int e = threadIdx.x; e < ng * (D / 4); e += NW * 64)
-        store4(p.o_part, orow0 * D + 4 * e, f32x4{0.f, 0.f, 0.f, 0.f}, p.odt);
-      if (threadIdx.x < ng) p.lse_part[orow0 + threadIdx.x] = neg_inf();
-    }
-    return;
-  }
   const int t_end = min(L, t_begin + p.chunk);
   const int nlive = (L + p.chunk - 1) / p.chunk;
 
@@ -155,8 +281,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     for (int s = 0; s < KS; ++s) qop[s] = (l16 < ng) ? ld16(qrow + 32 * s) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  const T* kb = static_cast<const T*>(p.k[r]) + b * p.sb + h * p.sh;
-  const T* vb = static_cast<const T*>(p.v[r]) + b * p.sb + h * p.sh;
+  const T* kb = static_cast<const T*>(kshard) + b * p.sb + h * p.sh;
+  const T* vb = static_cast<const T*>(vshard) + b * p.sb + h * p.sh;
   const int64_t st = p.st;
 
   float m = neg_inf();  // running max (base-2 units), uniform over q4
@@ -318,6 +444,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 
   if (nlive == 1) {
     if (wave == 0 && l16 < ng) {
+      const rsrc_t o_rs =
+          make_rsrc(p.o_part, (uint32_t)((int64_t)p.R * p.B * p.Hq * D * esize(p.odt)));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int d0 = 8 * (16 * nb + 4 * q4);
@@ -327,9 +455,18 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int n = 0; n < 8; ++n) y[8 * i + n] = acc[nb][n][i] * inv_l;
-        store32(p.o_part, (orow0 + l16) * D + d0, y, p.odt);
+        if constexpr (kDev)
+          store32_dev(o_rs, (uint32_t)(((orow0 + l16) * D + d0) * esize(p.odt)), y, p.odt);
+        else
+          store32(p.o_part, (orow0 + l16) * D + d0, y, p.odt);
       }
-      if (q4 == 0) p.lse_part[orow0 + l16] = lse_nat;
+      if (q4 == 0) {
+        if constexpr (kDev)
+          st4_dev(make_rsrc(p.lse_part, (uint32_t)((int64_t)p.R * p.B * p.Hq * 4)),
+                  (uint32_t)((orow0 + l16) * 4), lse_nat);
+        else
+          p.lse_part[orow0 + l16] = lse_nat;
+      }
     }
     return;
   }
@@ -337,6 +474,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
   // ---- several live chunks: this chunk's normalised partial to the workspace ----
   const int64_t slot = (int64_t)unit * p.nchunks + c;
   if (wave == 0 && l16 < ng) {
+    const int64_t nslots = (int64_t)p.units * p.nchunks * p.Gb;
+    const rsrc_t wo_rs = make_rsrc(p.ws_o, (uint32_t)(nslots * D * 4));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int d0 = 8 * (16 * nb + 4 * q4);
@@ -346,9 +485,388 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int n = 0; n < 8; ++n) y[8 * i + n] = acc[nb][n][i] * inv_l;
-      store32(p.ws_o, (slot * p.Gb + l16) * D + d0, y, kF32);
+      if constexpr (kDev)
+        store32_dev(wo_rs, (uint32_t)(((slot * p.Gb + l16) * D + d0) * 4), y, kF32);
+      else
+        store32(p.ws_o, (slot * p.Gb + l16) * D + d0, y, kF32);
     }
-    if (q4 == 0) p.ws_lse[slot * p.Gb + l16] = lse_nat;
+    if (q4 == 0) {
+      if constexpr (kDev)
+        st4_dev(make_rsrc(p.ws_lse, (uint32_t)(nslots * 4)), (uint32_t)((slot * p.Gb + l16) * 4),
+                lse_nat);
+      else
+        p.ws_lse[slot * p.Gb + l16] = lse_nat;
+    }
+  }
+}
+
+// Cross-shard weights of one group, one thread per (shard r, head g) pair:
+// ew = e^(lse_r - M_g) in FP64 with M_g the head's largest shard lse (0 for an
+// empty shard), and M_g itself.  Needs ms.lse; a barrier must follow.
+template <int NW, int MODE>
+__device__ __forceinline__ void shard_weights(int R, int ng, MergeSmem<NW, MODE>& ms) {
+  for (int pi = threadIdx.x; pi < R * ng; pi += NW * 64) {
+    const int g = pi % ng;
+    float M = neg_inf();
+    for (int r0 = 0; r0 < R; r0 += 8)  // 8 LDS reads in flight
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < R) M = fmaxf(M, ms.lse[(r0 + j) * ng + g]);
+    const float l = ms.lse[pi];
+    ms.ew[pi] = l == neg_inf() ? 0.0 : exp((double)l - (double)M);
+    if (pi < ng) ms.M[pi] = M;
+  }
+}
+
+// The cross-shard merge of output vector e (head g = e / (D/4)) from the
+// shard vectors y(r) (shard order, FP32 sums, FP64 weights and lse; every
+// shard empty: 0 and -inf).  Same arithmetic as the merge kernel.
+template <int D, typename YF, int NW, int MODE>
+__device__ __forceinline__ void merge_vector(const Args& p, int64_t row0, int e, int R, int ng,
+                                             const MergeSmem<NW, MODE>& ms, YF y) {
+  constexpr int Q = D / 4;
+  const int g = e / Q, qd = e % Q;
+  const int64_t row = row0 + g;
+  double S = 0.0;
+  for (int r0 = 0; r0 < R; r0 += 8)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (r0 + j < R) S += ms.ew[(r0 + j) * ng + g];
+  if (S == 0.0) {
+    store4(p.out, row * D + 4 * qd, f32x4{0.f, 0.f, 0.f, 0.f}, p.out_dt);
+    if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = neg_inf();
+    return;
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < R; r0 += 8)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + j;
+      if (r < R) {
+        const double ew = ms.ew[r * ng + g];
+        if (ew != 0.0) acc += (float)ew * y(r);
+      }
+    }
+  store4(p.out, row * D + 4 * qd, acc * (float)(1.0 / S), p.out_dt);
+  if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (float)((double)ms.M[g] + log(S));
+}
+
+// Merge of one (sequence, kv head, head block) group over its R shards when
+// shards are not split: every shard's o_part/lse_part rows were written by
+// the other workgroups of this launch with device-scope stores; empty shards
+// (no tokens) are never read.  s_nl[r] = live chunks (0 or 1) of shard r.
+// The shard vectors of this thread's first output vector are loaded together
+// with the lse values (one memory round trip).
+template <int D, int NW>
+__device__ void merge_shards(const Args& p, int b, int h, int gb, const int* s_nl,
+                             MergeSmem<NW, kStepOneShards>& ms) {
+  constexpr int NT = NW * 64;
+  constexpr int Q = D / 4;  // float4 outputs per head
+  constexpr int RB = 8;     // shard vectors loaded per batch
+  const int t = threadIdx.x;
+  const int g0 = gb * kGroupRows;
+  const int ng = min(kGroupRows, p.G - g0);
+  const int R = p.R;
+  const int E = ng * Q;
+  const uint32_t es = esize(p.odt);
+  const rsrc_t o_rs = make_rsrc(p.o_part, (uint32_t)((int64_t)R * p.B * p.Hq * D * es));
+  const rsrc_t l_rs = make_rsrc(p.lse_part, (uint32_t)((int64_t)R * p.B * p.Hq * 4));
+  const int64_t row0 = (int64_t)b * p.Hq + h * p.G + g0;  // out row of head 0
+  const int64_t rstride = (int64_t)p.B * p.Hq;             // o_part rows from shard to shard
+  auto vec_off = [&](int r, int e) {  // shard r's float4 e, out of range for an empty shard
+    return (e < E && r < R && s_nl[min(r, R - 1)] > 0)
+               ? (uint32_t)(((r * rstride + row0 + e / Q) * D + 4 * (e % Q)) * es)
+               : kOutOfRange;
+  };
+
+  float l_first = neg_inf();
+  if (t < R * ng) {
+    const int r = t / ng;
+    l_first = ld4f_dev(l_rs, s_nl[r] > 0 ? (uint32_t)((r * rstride + row0 + t % ng) * 4) : kOutOfRange);
+  }
+  f32x4 pre[RB];  // shards 0..RB-1 of output vector e = t
+#pragma unroll
+  for (int j = 0; j < RB; ++j) pre[j] = load4_dev(o_rs, vec_off(j, t), p.odt);
+
+  if (t < R * ng) ms.lse[t] = s_nl[t / ng] > 0 ? l_first : neg_inf();
+  for (int i = t + NT; i < R * ng; i += NT) {
+    const int r = i / ng;
+    const float v = ld4f_dev(l_rs, s_nl[r] > 0 ? (uint32_t)((r * rstride + row0 + i % ng) * 4) : kOutOfRange);
+    ms.lse[i] = s_nl[r] > 0 ? v : neg_inf();
+  }
+  __syncthreads();
+  shard_weights(R, ng, ms);
+  __syncthreads();
+
+  for (int e = t; e < E; e += NT) {
+    if (e == t && R <= RB) {  // the prefetched vectors, shard order (static indices)
+      const int g = e / Q, qd = e % Q;
+      const int64_t row = row0 + g;
+      double S = 0.0;
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        if (j < R) S += ms.ew[j * ng + g];
+      if (S == 0.0) {
+        store4(p.out, row * D + 4 * qd, f32x4{0.f, 0.f, 0.f, 0.f}, p.out_dt);
+        if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = neg_inf();
+        continue;
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        if (j >= R) break;
+        const double ew = ms.ew[j * ng + g];
+        if (ew != 0.0) acc += (float)ew * pre[j];
+      }
+      store4(p.out, row * D + 4 * qd, acc * (float)(1.0 / S), p.out_dt);
+      if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (float)((double)ms.M[g] + log(S));
+    } else {
+      merge_vector<D>(p, row0, e, R, ng, ms,
+                      [&](int r) { return load4_dev(o_rs, vec_off(r, e), p.odt); });
+    }
+  }
+}
+
+// Merge of one group when shards are split into chunks.  (1) One thread per
+// (shard, head) pair: the chunk lse of its live chunks, their max, weights
+// and sum (the chunk-combine arithmetic) and the shard lse.  (2) The FP64
+// cross-shard weights.  (3) Per (shard, output vector) the chunk sum, split
+// over P thread groups added in a fixed order, written to o_part.  (4) The
+// cross-shard merge of the stored shard vectors.  The first batch of (3)'s
+// loads is issued with (1)'s.  s_nl[r] = live chunks of shard r.
+template <int D, int NW>
+__device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_nl,
+                             MergeSmem<NW, kStepOneChunks>& ms) {
+  constexpr int NT = NW * 64;
+  constexpr int Q = D / 4;
+  constexpr int KB = 16;  // loads per batch
+  const int t = threadIdx.x;
+  const int g0 = gb * kGroupRows;
+  const int ng = min(kGroupRows, p.G - g0);
+  const int R = p.R;
+  const int nch = p.nchunks;
+  const uint32_t es = esize(p.odt);
+  const int64_t nslots = (int64_t)p.units * nch * p.Gb;
+  const rsrc_t o_rs = make_rsrc(p.o_part, (uint32_t)((int64_t)R * p.B * p.Hq * D * es));
+  const rsrc_t l_rs = make_rsrc(p.lse_part, (uint32_t)((int64_t)R * p.B * p.Hq * 4));
+  const rsrc_t wo_rs = make_rsrc(p.ws_o, (uint32_t)(nslots * D * 4));
+  const rsrc_t wl_rs = make_rsrc(p.ws_lse, (uint32_t)(nslots * 4));
+  const int64_t row0 = (int64_t)b * p.Hq + h * p.G + g0;  // out row of head 0
+  const int64_t rstride = (int64_t)p.B * p.Hq;
+  const int64_t ustride = (int64_t)p.B * p.Hkv * p.gblocks;  // units from shard to shard
+  const int64_t slot00 = (int64_t)((b * p.Hkv + h) * p.gblocks + gb) * nch;  // shard 0, chunk 0
+  const uint32_t cstride = (uint32_t)(p.Gb * D * 4);  // workspace bytes from chunk to chunk
+
+  // (3)'s work split: items = (shard, float4) pairs, P chunk partitions each
+  const int E = ng * Q;
+  const int items = R * E;
+  int P = 1;
+  while (P < 8 && items * P * 2 <= NT) P *= 2;
+  const int per = NT / P;
+  const int part_id = t / per;
+  auto vec_base = [&](int r, int e) {  // chunk 0 of shard r's float4 e in the workspace
+    return (uint32_t)(((slot00 + r * ustride * nch) * p.Gb + e / Q) * D * 4) + 16u * (e % Q);
+  };
+
+  // ---- prefetch the first batch of this thread's first item ----
+  const int it_first = t % per;
+  const int r_first = min(it_first / E, R - 1), e_first = it_first % E;
+  const int nl_first = it_first < items ? s_nl[r_first] : 0;
+  f32x4 pre[KB];
+  {
+    const uint32_t base = vec_base(r_first, e_first);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int cc = part_id + j * P;
+      pre[j] = __builtin_bit_cast(
+          f32x4, ld16_dev(wo_rs, (nl_first >= 2 && cc < nl_first) ? base + cc * cstride : kOutOfRange));
+    }
+  }
+  const f32x4 pre_one = load4_dev(
+      o_rs,
+      (nl_first == 1 && part_id == 0)
+          ? (uint32_t)(((r_first * rstride + row0 + e_first / Q) * D + 4 * (e_first % Q)) * es)
+          : kOutOfRange,
+      p.odt);
+
+  // (1) per (shard, head): chunk weights and shard lse
+  for (int pi = t; pi < R * ng; pi += NT) {
+    const int r = pi / ng, g = pi - r * ng;
+    const int nl = s_nl[r];
+    float l = neg_inf();
+    if (nl == 1) {
+      l = ld4f_dev(l_rs, (uint32_t)((r * rstride + row0 + g) * 4));
+    } else if (nl >= 2) {
+      float* wr = ms.w + pi * nch;
+      const uint32_t lbase = (uint32_t)(((slot00 + r * ustride * nch) * p.Gb + g) * 4);
+      const uint32_t lstride = (uint32_t)(p.Gb * 4);
+      constexpr int LB = 16;  // chunks held in registers
+      float v[LB];
+#pragma unroll
+      for (int j = 0; j < LB; ++j) v[j] = ld4f_dev(wl_rs, j < nl ? lbase + j * lstride : kOutOfRange);
+      float M = neg_inf();
+      float S = 0.f;
+      if (nl <= LB) {  // all in registers
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+          if (j < nl) M = fmaxf(M, v[j]);
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+          v[j] = j < nl ? expf(v[j] - M) : 0.f;
+          S += v[j];
+        }
+        const float invS = 1.0f / S;
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+          if (j < nl) wr[j] = v[j] * invS;
+      } else {  // through LDS, in chunk order
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+          wr[j] = v[j];
+          M = fmaxf(M, v[j]);
+        }
+        for (int c = LB; c < nl; ++c) {
+          wr[c] = ld4f_dev(wl_rs, lbase + c * lstride);
+          M = fmaxf(M, wr[c]);
+        }
+        for (int c = 0; c < nl; ++c) {
+          const float e = expf(wr[c] - M);
+          wr[c] = e;
+          S += e;
+        }
+        const float invS = 1.0f / S;
+        for (int c = 0; c < nl; ++c) wr[c] *= invS;
+      }
+      l = M + logf(S);
+      p.lse_part[r * rstride + row0 + g] = l;
+    }
+    ms.lse[pi] = l;
+  }
+  __syncthreads();
+  shard_weights(R, ng, ms);  // (2); read only after the next barrier
+
+  // (3) every shard's partial vectors
+  for (int i0 = 0; i0 < items; i0 += per) {
+    const int it = i0 + t % per;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    int r = 0, e = 0, nl = 0;
+    if (it < items) {
+      r = it / E;
+      e = it - r * E;
+      nl = s_nl[r];
+      if (nl >= 2) {
+        const float* wr = ms.w + (r * ng + e / Q) * nch;
+        const uint32_t base = vec_base(r, e);
+        int c0 = part_id;
+        if (i0 == 0) {  // the prefetched first batch
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            const int cc = c0 + j * P;
+            if (cc < nl) y += wr[cc] * pre[j];
+          }
+          c0 += KB * P;
+        }
+        for (; c0 < nl; c0 += KB * P) {
+          f32x4 v[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            const int cc = c0 + j * P;
+            v[j] = __builtin_bit_cast(f32x4, ld16_dev(wo_rs, cc < nl ? base + cc * cstride : kOutOfRange));
+          }
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            const int cc = c0 + j * P;
+            if (cc < nl) y += wr[cc] * v[j];
+          }
+        }
+      } else if (nl == 1 && part_id == 0) {
+        y = i0 == 0 ? pre_one
+                    : load4_dev(o_rs, (uint32_t)(((r * rstride + row0 + e / Q) * D + 4 * (e % Q)) * es),
+                                p.odt);
+      }
+    }
+    if (P > 1) {
+      ms.part[t] = y;
+      __syncthreads();
+      if (part_id == 0 && it < items)
+        for (int q = 1; q < P; ++q) y += ms.part[t + q * per];
+      __syncthreads();
+    }
+    if (part_id == 0 && it < items) {
+      if (nl >= 2) {
+        store4(p.o_part, (r * rstride + row0 + e / Q) * D + 4 * (e % Q), y, p.odt);
+        y = round4(y, p.odt);
+      }
+      ms.y[it] = y;
+    }
+  }
+  __syncthreads();
+
+  // (4) cross-shard merge
+  for (int e = t; e < E; e += NT)
+    merge_vector<D>(p, row0, e, R, ng, ms, [&](int r) { return ms.y[r * E + e]; });
+}
+
+template <typename T, int D, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
+  const Args p = load_args(kp);
+  __shared__ KernelSmem<T, D, NW, MODE> sh;
+  __shared__ int s_last;
+  __shared__ int s_nl[MODE >= kStepOneShards ? kMaxShards : 1];  // live chunks per shard
+
+  // Chunk-major order: workgroups are dealt to the 8 XCDs round-robin by
+  // block index, so block % 8 must not correlate with the chunk index (the
+  // later chunks of ragged shards are mostly empty); here it follows the unit.
+  const int c = blockIdx.x / p.units;
+  const int unit = blockIdx.x % p.units;
+  int u = unit;
+  const int gb = u % p.gblocks; u /= p.gblocks;
+  const int h = u % p.Hkv; u /= p.Hkv;
+  const int b = u % p.B;
+  const int r = u / p.B;
+  const int L = __builtin_amdgcn_readfirstlane(p.lens[r * p.B + b]);  // uniform address
+  // One-launch step: every shard's length of this sequence, for whichever
+  // workgroup ends up merging (issued now, used after the attention).
+  int len_t = 0;
+  if constexpr (MODE >= kStepOneShards) {
+    const rsrc_t lens_rs = make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4));
+    len_t = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        lens_rs, threadIdx.x < (unsigned)p.R ? (int)((threadIdx.x * p.B + b) * 4) : (int)kOutOfRange, 0,
+        0);
+  }
+
+  if (c * p.chunk < L) {
+    attend_chunk<T, D, NW, MODE>(p, kp.k[r], kp.v[r], sh.a, c, unit, r, b, h, gb, L);
+  } else if (c == 0) {  // empty shard: o_r = 0, lse_r = -inf (the merge never reads them)
+    const int g0 = gb * kGroupRows;
+    const int ng = min(kGroupRows, p.G - g0);
+    const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
+    for (int e = threadIdx.x; e < ng * (D / 4); e += NW * 64)
+      store4(p.o_part, orow0 * D + 4 * e, f32x4{0.f, 0.f, 0.f, 0.f}, p.odt);
+    if (threadIdx.x < ng) p.lse_part[orow0 + threadIdx.x] = neg_inf();
+  }
+  if constexpr (MODE >= kStepOneShards) {
+    // Arrival: this workgroup's device-scope stores are complete before the
+    // counter moves; the workgroup that takes the group's counter to its
+    // member count (R shards x chunks) merges the group and resets it.
+    if (threadIdx.x < (unsigned)p.R) s_nl[threadIdx.x] = (len_t + p.chunk - 1) / p.chunk;
+    wait_vm_all();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int grp = ((b * p.Hkv + h) * p.gblocks + gb) * kStepCounterStride;
+      const int members = p.R * p.nchunks;
+      const int old =
+          __hip_atomic_fetch_add(p.counters + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == members - 1;
+      if (last) __hip_atomic_store(p.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if constexpr (MODE == kStepOneShards)
+      merge_shards<D, NW>(p, b, h, gb, s_nl, sh.m);
+    else
+      merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
   }
 }
 
@@ -359,7 +877,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 // fewer than 256 float4 outputs, and the groups are added in a fixed order
 // (results do not depend on timing).
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) {
+  const Args p = load_args(kp);
   __shared__ float w[kMaxChunks][16];
   __shared__ f32x4 part[256];
   const int unit = blockIdx.x;
@@ -368,7 +887,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const int h = u % p.Hkv; u /= p.Hkv;
   const int b = u % p.B;
   const int r = u / p.B;
-  const int L = p.lens[r * p.B + b];
+  const int L = __builtin_amdgcn_readfirstlane(p.lens[r * p.B + b]);  // uniform address
   const int nlive = (L + p.chunk - 1) / p.chunk;
   if (nlive < 2) return;  // written directly by the attention kernel
   const int g0 = gb * kGroupRows;
@@ -428,186 +947,49 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
 }
 
-// The whole step's second launch, for one (sequence, kv head, head block)
-// and all R shards at once: (1) per (shard, head) the chunk weights (wave
-// reductions), (2) per (shard, output vector) the shard's partial -- merged
-// from its chunks and written to o_part, or read back when the attention
-// kernel wrote it (0 or 1 live chunk) -- kept in LDS, (3) the cross-shard
-// merge in shard order (FP64 weights and lse, FP32 sums, -inf shards
-// skipped) into out/lse_out.  Used when the per-shard state fits LDS
-// (kFusedChunkSlots, kFusedVecs); otherwise the separate kernels run.
-constexpr int kFusedChunkSlots = 512;  // R * chunks
-constexpr int kFusedVecs = 1024;       // R * (heads * D / 4)
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine_merge_kernel(const AttnParams p, void* out,
-                                                                 float* lse_out, int out_dt) {
-  __shared__ float w[kFusedChunkSlots][16];
-  __shared__ f32x4 ybuf[kFusedVecs];
-  __shared__ f32x4 part[256];
-  __shared__ float s_lse[kMaxShards][16];
-  __shared__ int s_nlive[kMaxShards];
-  const int bh = blockIdx.x;  // ((b * Hkv) + h) * gblocks + gb
-  const int gb = bh % p.gblocks;
-  const int h = (bh / p.gblocks) % p.Hkv;
-  const int b = bh / (p.gblocks * p.Hkv);
-  const int g0 = gb * kGroupRows;
-  const int ng = min(kGroupRows, p.G - g0);
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int t = threadIdx.x;
-  const int R = p.R;
-  auto unit_of = [&](int r) { return ((r * p.B + b) * p.Hkv + h) * p.gblocks + gb; };
-  auto orow_of = [&](int r) { return ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0; };
-
-  if (t < R) {
-    const int L = p.lens[t * p.B + b];
-    s_nlive[t] = (L + p.chunk - 1) / p.chunk;
-  }
-  __syncthreads();
-
-  // (1) chunk weights and shard lse, one (shard, head) pair per wave in turn
-  for (int pi = wave; pi < R * ng; pi += 4) {
-    const int r = pi / ng, g = pi % ng;
-    const int nlive = s_nlive[r];
-    if (nlive < 2) {  // 0 or 1 live chunk: the attention kernel wrote lse_part
-      if (lane == 0) s_lse[r][g] = p.lse_part[orow_of(r) + g];
-      continue;
-    }
-    const int64_t slot0 = (int64_t)unit_of(r) * p.nchunks;
-    float M = neg_inf();
-    for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float S = 0.f;
-    for (int cc = lane; cc < nlive; cc += 64) {
-      const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
-      w[r * p.nchunks + cc][g] = e;
-      S += e;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-    const float invS = 1.0f / S;
-    for (int cc = lane; cc < nlive; cc += 64) w[r * p.nchunks + cc][g] *= invS;
-    if (lane == 0) {
-      const float l = M + logf(S);
-      p.lse_part[orow_of(r) + g] = l;
-      s_lse[r][g] = l;
-    }
-  }
-  __syncthreads();
-
-  // (2) every shard's partial vectors (chunks split over P thread groups)
-  constexpr int Q = D / 4;               // float4 outputs per head
-  const int E = ng * Q;                  // float4 outputs per shard
-  const int items = R * E;
-  int P = 1;
-  while (P < 8 && items * P * 2 <= 256) P *= 2;
-  const int per = 256 / P;
-  const int part_id = t / per;
-  for (int i0 = 0; i0 < items; i0 += per) {
-    const int it = i0 + t % per;
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    int r = 0, e = 0, nlive = 0;
-    if (it < items) {
-      r = it / E;
-      e = it % E;
-      nlive = s_nlive[r];
-      const int g = e / Q;
-      if (nlive >= 2) {
-        const int64_t slot0 = (int64_t)unit_of(r) * p.nchunks;
-        const float* src = p.ws_o + (slot0 * p.Gb + g) * D + 4 * (e % Q);
-        const int64_t cstride = (int64_t)p.Gb * D;
-#pragma unroll 4
-        for (int cc = part_id; cc < nlive; cc += P)
-          y += w[r * p.nchunks + cc][g] * *reinterpret_cast<const f32x4*>(src + cc * cstride);
-      } else if (nlive == 1 && part_id == 0) {
-        y = load4(p.o_part, (orow_of(r) + g) * D + 4 * (e % Q), p.odt);
-      }
-    }
-    if (P > 1) {
-      part[t] = y;
-      __syncthreads();
-      if (part_id == 0 && it < items)
-        for (int q = 1; q < P; ++q) y += part[t + q * per];
-      __syncthreads();
-    }
-    if (part_id == 0 && it < items) {
-      if (nlive >= 2) store4(p.o_part, (orow_of(r) + e / Q) * D + 4 * (e % Q), y, p.odt);
-      ybuf[it] = y;
-    }
-  }
-  __syncthreads();
-
-  // (3) cross-shard merge in shard order
-  for (int e = t; e < E; e += 256) {
-    const int g = e / Q;
-    float M = neg_inf();
-    for (int r = 0; r < R; ++r) M = fmaxf(M, s_lse[r][g]);
-    const int64_t row = (int64_t)b * p.Hq + h * p.G + g0 + g;
-    if (M == neg_inf()) {
-      store4(out, row * D + 4 * (e % Q), f32x4{0.f, 0.f, 0.f, 0.f}, out_dt);
-      if (lse_out != nullptr && e % Q == 0) lse_out[row] = neg_inf();
-      continue;
-    }
-    double S = 0.0;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < R; ++r) {
-      const float l = s_lse[r][g];
-      if (l == neg_inf()) continue;  // empty shard: never used
-      const double ew = exp((double)l - (double)M);
-      S += ew;
-      acc += (float)ew * ybuf[r * E + e];
-    }
-    store4(out, row * D + 4 * (e % Q), acc * (float)(1.0 / S), out_dt);
-    if (lse_out != nullptr && e % Q == 0) lse_out[row] = (float)((double)M + log(S));
-  }
-}
-
 template <typename T, int D, int NW>
-hipError_t launch_typed(const AttnParams& p, int64_t units, const StepOut* so, hipStream_t s) {
-  const int64_t blocks = units * p.nchunks;
-  hipLaunchKernelGGL((attn_partial_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, s,
-                     p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t fused_vecs = (int64_t)p.R * p.Gb * (D / 4);
-  if (so != nullptr && p.nchunks >= 2 && (int64_t)p.R * p.nchunks <= kFusedChunkSlots &&
-      fused_vecs <= kFusedVecs) {  // the whole step: chunk merge + shard merge fused
-    hipLaunchKernelGGL((attn_combine_merge_kernel<D>), dim3((unsigned)(units / p.R)), dim3(256), 0,
-                       s, p, so->out, so->lse_out, so->out_dt);
+hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipStream_t s) {
+  const dim3 grid((unsigned)(units * p.nchunks)), block(NW * 64);
+  if (mode == kStepOneShards) {
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneShards>), grid, block, 0, s, p);
     return hipGetLastError();
   }
+  if (mode == kStepOneChunks) {
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (p.nchunks >= 2) {
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (so != nullptr)  // the whole step, unsplit: the cross-shard merge reads o_part
-    return launch_lse_merge(p.o_part, p.lse_part, p.R, (int64_t)p.B * p.Hq, D, p.odt, so->out_dt,
-                            so->out, so->lse_out, s);
+  if (mode == kStepLaunches)  // the cross-shard merge reads o_part
+    return launch_lse_merge(p.o_part, p.lse_part, p.R, (int64_t)p.B * p.Hq, D, p.odt, p.out_dt,
+                            p.out, p.lse_out, s);
   return hipSuccess;
 }
 
 template <typename T, int D>
-hipError_t launch_w(const AttnParams& p, int waves, int64_t units, const StepOut* so,
-                    hipStream_t s) {
+hipError_t launch_w(const AttnParams& p, int waves, int64_t units, StepMode mode, hipStream_t s) {
   switch (waves) {
-    case 1: return launch_typed<T, D, 1>(p, units, so, s);
-    case 2: return launch_typed<T, D, 2>(p, units, so, s);
-    case 4: return launch_typed<T, D, 4>(p, units, so, s);
-    case 8: return launch_typed<T, D, 8>(p, units, so, s);
+    case 1: return launch_typed<T, D, 1>(p, units, mode, s);
+    case 2: return launch_typed<T, D, 2>(p, units, mode, s);
+    case 4: return launch_typed<T, D, 4>(p, units, mode, s);
+    case 8: return launch_typed<T, D, 8>(p, units, mode, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_d(const AttnParams& p, int D, int waves, int64_t units, const StepOut* so,
+hipError_t launch_d(const AttnParams& p, int D, int waves, int64_t units, StepMode mode,
                     hipStream_t s) {
   switch (D) {
-    case 64: return launch_w<T, 64>(p, waves, units, so, s);
-    case 128: return launch_w<T, 128>(p, waves, units, so, s);
-    case 256: return launch_w<T, 256>(p, waves, units, so, s);
+    case 64: return launch_w<T, 64>(p, waves, units, mode, s);
+    case 128: return launch_w<T, 128>(p, waves, units, mode, s);
+    case 256: return launch_w<T, 256>(p, waves, units, mode, s);
   }
   return hipErrorInvalidValue;
 }
@@ -625,9 +1007,9 @@ __global__ void clear_tail_kernel(unsigned char* q, size_t n) {
 }  // namespace
 
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves, int64_t units,
-                               const StepOut* so, hipStream_t s) {
-  if (qkv_dt == kBF16) return launch_d<bf16_t>(p, D, waves, units, so, s);
-  if (qkv_dt == kF16) return launch_d<f16_t>(p, D, waves, units, so, s);
+                               StepMode mode, hipStream_t s) {
+  if (qkv_dt == kBF16) return launch_d<bf16_t>(p, D, waves, units, mode, s);
+  if (qkv_dt == kF16) return launch_d<f16_t>(p, D, waves, units, mode, s);
   return hipErrorInvalidValue;
 }
 

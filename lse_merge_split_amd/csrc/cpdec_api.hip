@@ -8,6 +8,8 @@
 #include "cpdec.h"
 #include "kernels.h"
 
+static_assert(cpdec::kStepCounterBytes == CPDEC_STEP_COUNTER_BYTES, "counter region size");
+
 namespace {
 
 using namespace cpdec;
@@ -21,7 +23,9 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Overrides {
   int waves = 0;   // CPDEC_WAVES: 1, 2, 4 or 8
   int chunk = 0;   // CPDEC_CHUNK: tokens, multiple of 32
+  bool step_launches = false;  // CPDEC_STEP_LAUNCHES=1: the whole step as separate launches
   Overrides() {
+    if (const char* s = getenv("CPDEC_STEP_LAUNCHES")) step_launches = atoi(s) != 0;
     if (const char* s = getenv("CPDEC_WAVES")) {
       int w = atoi(s);
       if (w == 1 || w == 2 || w == 4 || w == 8) waves = w;
@@ -48,7 +52,10 @@ struct AttnPlan {
   int nchunks = 0;
   int G = 0, Gb = 0, gblocks = 0;
   int64_t units = 0;
-  size_t ws_bytes = 0, off_lse = 0, off_o = 0;
+  size_t ws_bytes = 0;       // what cpdec_attn_partial needs (0: no workspace)
+  size_t step_ws_bytes = 0;  // what cpdec_cp_decode needs (counters + partials)
+  size_t off_lse = 0, off_o = 0;
+  StepMode step = kStepLaunches;  // how cpdec_cp_decode runs
 };
 
 // Validate a descriptor (no pointers) and plan the launch.
@@ -108,12 +115,30 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
       (int64_t)d->num_shards * d->batch * d->num_q_heads > INT32_MAX)
     return CPDEC_ERR_INVALID_ARG;
 
+  // Workspace: the whole step's arrival counters first (at a fixed offset, so
+  // calls of any shape that share a workspace never overwrite them), then the
+  // chunk partials.
+  const size_t slots = (size_t)p.units * p.nchunks * p.Gb;
   if (p.nchunks > 1) {
-    const size_t slots = (size_t)p.units * p.nchunks * p.Gb;
-    p.off_lse = 0;
-    p.off_o = round256(slots * sizeof(float));
+    p.off_lse = kStepCounterBytes;
+    p.off_o = p.off_lse + round256(slots * sizeof(float));
     p.ws_bytes = p.off_o + slots * (size_t)D * sizeof(float);
   }
+  p.step_ws_bytes = p.ws_bytes > kStepCounterBytes ? p.ws_bytes : kStepCounterBytes;
+
+  // The whole step in one launch when the counters, the merging workgroup's
+  // LDS and 32-bit buffer offsets allow it.
+  const int64_t groups = (int64_t)d->batch * d->num_kv_heads * p.gblocks;
+  const uint64_t opart_bytes = (uint64_t)d->num_shards * d->batch * d->num_q_heads * D *
+                               (d->opart_dtype == CPDEC_F32 ? 4u : 2u);
+  bool one = !overrides().step_launches && groups <= kStepCounters && opart_bytes < (1ull << 31);
+  if (p.nchunks > 1)
+    one = one && (int64_t)d->num_shards * p.nchunks * p.Gb <= kStepSlots &&
+          (int64_t)d->num_shards * p.Gb * (D / 4) <= kStepVecs &&
+          slots * (size_t)D * sizeof(float) < (1ull << 31);
+  else  // large unsplit grids: a merge launch costs less than write-through o_part stores
+    one = one && p.units <= kStepUnsplitBlocks;
+  p.step = !one ? kStepLaunches : (p.nchunks > 1 ? kStepOneChunks : kStepOneShards);
   *pl = p;
   return CPDEC_OK;
 }
@@ -130,6 +155,20 @@ size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d) {
   return pl.ws_bytes;
 }
 
+size_t cpdec_step_workspace_bytes(const cpdec_attn_desc* d) {
+  AttnPlan pl;
+  if (plan_attn(d, &pl) != CPDEC_OK) return 0;
+  return pl.step_ws_bytes;
+}
+
+cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches) {
+  AttnPlan pl;
+  const cpdec_status st = plan_attn(d, &pl);
+  if (st != CPDEC_OK) return st;
+  if (launches) *launches = pl.step != kStepLaunches ? 1 : (pl.nchunks > 1 ? 3 : 2);
+  return CPDEC_OK;
+}
+
 cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens, int32_t* num_chunks,
                              int32_t* waves) {
   AttnPlan pl;
@@ -140,6 +179,12 @@ cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens, in
   if (waves) *waves = pl.waves;
   return CPDEC_OK;
 }
+
+struct StepOut {
+  void* out;
+  float* lse_out;
+  int out_dt;
+};
 
 static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
                                 const void* const* k_shards, const void* const* v_shards,
@@ -185,8 +230,9 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
     return CPDEC_ERR_ALIGNMENT;
   for (int r = 0; r < d->num_shards; ++r)
     if (!aligned16(k_shards[r]) || !aligned16(v_shards[r])) return CPDEC_ERR_ALIGNMENT;
-  if (pl.ws_bytes > 0) {
-    if (workspace == nullptr || workspace_bytes < pl.ws_bytes ||
+  const size_t need = so != nullptr ? pl.step_ws_bytes : pl.ws_bytes;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
       return CPDEC_ERR_WORKSPACE;
   }
@@ -206,6 +252,14 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
     p.ws_lse = reinterpret_cast<float*>(ws + pl.off_lse);
     p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   }
+  StepMode mode = kPartialsOnly;
+  if (so != nullptr) {
+    mode = pl.step;
+    p.out = so->out;
+    p.lse_out = so->lse_out;
+    p.out_dt = so->out_dt;
+    p.counters = static_cast<int32_t*>(workspace);
+  }
   p.sb = d->kv_stride_batch;
   p.sh = d->kv_stride_head;
   p.st = d->kv_stride_token;
@@ -223,7 +277,7 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
   const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
 
-  hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units, so,
+  hipError_t e = launch_attn_partial(p, d->qkv_dtype, d->head_dim, pl.waves, pl.units, mode,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CPDEC_OK : CPDEC_ERR_HIP;
 }

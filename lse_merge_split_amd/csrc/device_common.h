@@ -110,4 +110,34 @@ __device__ __forceinline__ float buf4f(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// ---- hand-off between workgroups of one launch ---------------------------
+// Cache-policy bit sc1 (device scope).  A device-scope store is written
+// through to the level that every XCD's device-scope loads read, and a
+// device-scope load is served from there; the compiler emits exactly these
+// accesses for relaxed agent-scope atomic loads and stores.  A workgroup that
+// writes its result this way, waits for the stores to complete and then bumps
+// an agent-scope atomic counter has made the result visible to the workgroup
+// that sees the counter's last increment, without the L2 writeback and
+// invalidate of a device-scope fence (which costs microseconds per workgroup).
+constexpr int kPolicyDevice = 16;
+__device__ __forceinline__ void st16_dev(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ void st4_dev(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ u32x4 ld16_dev(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyDevice));
+}
+__device__ __forceinline__ u32x2 ld8_dev(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyDevice));
+}
+__device__ __forceinline__ float ld4f_dev(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyDevice));
+}
+// Wait until every memory access this wave issued has completed: s_waitcnt
+// vmcnt(0) expcnt(7) lgkmcnt(15) in the gfx9 encoding.  (A workgroup barrier
+// alone does not wait for outstanding global stores.)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace cpdec

@@ -26,21 +26,37 @@ struct AttnParams {
   int64_t sb, sh, st; // K/V element strides: batch, head, token
   int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt;
   float scale_log2;   // sm_scale * log2(e)
+  // the whole step (cpdec_cp_decode) only:
+  void* out;          // [B][Hq][D] merged output, dtype out_dt
+  float* lse_out;     // [B][Hq] merged lse, may be null
+  int32_t out_dt;
+  int32_t* counters;  // [B * Hkv * gblocks] arrival counters, zero between calls
 };
 
-// Where the whole step (cpdec_cp_decode) writes the merged result.
-struct StepOut {
-  void* out;
-  float* lse_out;  // may be null
-  int out_dt;
+// How a launch treats the cross-shard merge.
+enum StepMode : int {
+  kPartialsOnly = 0,   // cpdec_attn_partial: o_part/lse_part only
+  kStepLaunches = 1,   // whole step as attention, chunk combine and merge launches
+  kStepOneShards = 2,  // whole step in one launch, shards not split: the last
+                       // shard workgroup of a (sequence, kv head) merges
+  kStepOneChunks = 3,  // whole step in one launch, shards split into chunks:
+                       // the last chunk workgroup combines chunks and merges
 };
 
-// Launch the partial-attention kernel over units x nchunks workgroups, then
-// (when a unit can span several chunks) the chunk-combine kernel over units.
-// With `so` the cross-shard merge follows: fused into the chunk merge when
-// shards are split, else the plain merge kernel (two launches either way).
+// Limits of the one-launch step (the merging workgroup's LDS and counters).
+constexpr size_t kStepCounterBytes = 65536; // counters at the start of the workspace
+constexpr int kStepCounterStride = 16;      // ints: one 64-byte line per counter (atomics
+                                            // on one line serialise across groups)
+constexpr int kStepCounters = (int)(kStepCounterBytes / 4 / kStepCounterStride);  // groups
+constexpr int kStepSlots = 2048;            // shards * chunks * heads of one group
+constexpr int kStepVecs = 2048;             // shards * heads * D/4 of one group
+constexpr int64_t kStepUnsplitBlocks = 1024; // unsplit shards: one launch up to this grid
+
+// Launch the partial-attention kernel over units x nchunks workgroups and
+// whatever else `mode` needs (chunk combine and merge kernels for
+// kPartialsOnly/kStepLaunches; nothing for the one-launch modes).
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
-                               int64_t units, const StepOut* so, hipStream_t s);
+                               int64_t units, StepMode mode, hipStream_t s);
 
 hipError_t launch_lse_merge(const void* o, const float* lse, int R, int64_t rows, int D,
                             int in_dt, int out_dt, void* out, float* lse_out, hipStream_t s);

@@ -49,14 +49,35 @@ def _desc(**kw):
 
 def test_workspace_bytes():
     lib = cp.lib()
+    C = cp.STEP_COUNTER_BYTES
     one = _desc(chunk_tokens=1024)   # a single chunk covers the capacity
     assert lib.cpdec_attn_workspace_bytes(ctypes.byref(one)) == 0
-    split = _desc(chunk_tokens=128)  # 8 chunks -> counters + partials
+    assert lib.cpdec_step_workspace_bytes(ctypes.byref(one)) == C  # counters only
+    split = _desc(chunk_tokens=128)  # 8 chunks -> partials after the counter region
     nb = lib.cpdec_attn_workspace_bytes(ctypes.byref(split))
     units, nch, Gb, D = 4 * 2 * 2, 8, 4, 128
-    assert nb >= units * nch * Gb * (D + 1) * 4
-    assert lib.cpdec_attn_workspace_bytes(None) == 0
-    assert lib.cpdec_attn_workspace_bytes(ctypes.byref(_desc(head_dim=96))) == 0
+    assert nb >= C + units * nch * Gb * (D + 1) * 4
+    assert lib.cpdec_step_workspace_bytes(ctypes.byref(split)) == nb
+    for f in (lib.cpdec_attn_workspace_bytes, lib.cpdec_step_workspace_bytes):
+        assert f(None) == 0
+        assert f(ctypes.byref(_desc(head_dim=96))) == 0
+
+
+def test_step_plan_launches():
+    assert cp.step_launches(_desc(chunk_tokens=1024)) == 1     # shards merged in the launch
+    assert cp.step_launches(_desc(chunk_tokens=128)) == 1      # chunks and shards in the launch
+    # 4 shards x 16 heads x 256/4 vectors exceed the merging workgroup's LDS
+    wide = dict(num_q_heads=32, num_kv_heads=2, head_dim=256, kv_stride_token=256,
+                kv_stride_head=1000 * 256, kv_stride_batch=2 * 1000 * 256)
+    assert cp.step_launches(_desc(chunk_tokens=128, **wide)) == 3  # attention, combine, merge
+    assert cp.step_launches(_desc(chunk_tokens=1024, **wide)) == 1
+    # more (sequence, kv head) groups than counters
+    many = dict(batch=8193, kv_stride_batch=2 * 1000 * 128)
+    assert cp.step_launches(_desc(chunk_tokens=1024, **many)) == 2  # attention, merge
+    n = ctypes.c_int32(-1)
+    assert cp.lib().cpdec_step_plan(ctypes.byref(_desc(head_dim=96)), ctypes.byref(n)) == UNSUPPORTED
+    assert n.value == -1
+    assert cp.lib().cpdec_step_plan(None, None) == INVALID
 
 
 # Fake (never dereferenced) device addresses.  Every call below must fail
@@ -134,6 +155,10 @@ def test_cp_decode_errors():
     assert f(ctypes.byref(bad), A, ks, ks, A, A, A, A, A, None, 0, None) == UNSUPPORTED
     split = _desc(chunk_tokens=128)
     assert f(ctypes.byref(split), A, ks, ks, A, A, A, A, A, None, 0, None) == WS
+    # the whole step needs the counter region even when nothing is split
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, None, 0, None) == WS
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, A, cp.STEP_COUNTER_BYTES - 1, None) == WS
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, A + 16, cp.STEP_COUNTER_BYTES, None) == WS
 
 
 @needs_cpu_host

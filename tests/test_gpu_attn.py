@@ -266,7 +266,26 @@ def _full(name, groups_fn):
     assert np.all(lse_out[anylive] <= Mx[anylive] + np.log(nl[anylive]) + 1e-5 * np.abs(Mx[anylive]))
     _say(f"attn full {name}: oracle on sampled groups")
     check_groups(w, inp, res, groups_fn(w, lens))
-    del inp, res
+    # the whole step (one launch) on the same inputs
+    _say(f"attn full {name}: whole step")
+    step = {k: torch.empty_like(v) for k, v in res.items()}
+    desc = cp.make_attn_desc(inp["q"], inp["k_shards"])
+    print(f"[info] whole step: {cp.step_launches(desc)} launch(es)", flush=True)
+    ws = torch.zeros(cp.step_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], step["o_part"],
+                 step["lse_part"], step["out"], step["lse_out"], workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:cp.STEP_COUNTER_BYTES]).item()) == 0
+    assert torch.equal(torch.isneginf(step["lse_part"]), torch.isneginf(res["lse_part"]))
+    fin = torch.isfinite(res["lse_part"])
+    assert torch.allclose(step["lse_part"][fin], res["lse_part"][fin], rtol=1e-6, atol=1e-6)
+    assert torch.allclose(step["o_part"], res["o_part"], rtol=1e-5, atol=1e-6)
+    assert np.array_equal(np.isneginf(to64(step["lse_out"])), ~anylive)
+    # against the two calls: one output rounding apart at most
+    d = (step["out"].float() - res["out"].float()).abs()
+    assert bool((d <= 2.0 ** -7 * res["out"].float().abs() + 1e-6).all())
+    check_groups(w, inp, step, groups_fn(w, lens))
+    del inp, res, step
     torch.cuda.empty_cache()
 
 

@@ -18,6 +18,8 @@ from synth import gpu as sg  # noqa: E402
     ("split shards (chunk merge)", sc.small("c4", B=8, Lcap=700)),
     ("whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
     ("merge-only rows", None),
+    ("one-launch step, split", sc.small("c4", B=2, Lcap=700)),
+    ("one-launch step, whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
 ])
 def test_graph_replay_matches_eager(name, w):
     print(f"[case] graph replay: {name}", flush=True)
@@ -33,6 +35,23 @@ def test_graph_replay_matches_eager(name, w):
         cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
         refs = [ref_out, ref_lo]
         eager_work = lambda: cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
+    elif name.startswith("one-launch step"):
+        inp = sg.attn_inputs(w)
+        R, B, Hq, D = w.R, w.B, w.Hq, w.D
+        mk = lambda: (torch.empty((R, B, Hq, D), dtype=torch.float32, device="cuda"),
+                      torch.empty((R, B, Hq), dtype=torch.float32, device="cuda"),
+                      torch.empty((B, Hq, D), dtype=inp["q"].dtype, device="cuda"),
+                      torch.empty((B, Hq), dtype=torch.float32, device="cuda"))
+        desc = cp.make_attn_desc(inp["q"], inp["k_shards"])
+        assert cp.step_launches(desc) == 1
+        refs = list(mk())
+        cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], *refs)
+        outs = list(mk())
+        ws = torch.zeros(cp.step_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        calls = [cp.StepCall(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], *outs,
+                             workspace=ws)]
+        eager_work = lambda: cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"],
+                                          *mk())
     else:
         inp = sg.attn_inputs(w)
         ref = run_path(inp)

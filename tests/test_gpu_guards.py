@@ -49,10 +49,11 @@ def test_outputs_stay_in_bounds(name, w, chunk):
     bufs["out"], out = guarded((B, Hq, D), dt)
     bufs["lse_out"], lse_out = guarded((B, Hq), torch.float32)
     desc = cp.make_attn_desc(inp["q"], inp["k_shards"], chunk_tokens=chunk)
-    nws = max(cp.attn_workspace_bytes(desc), 256)
+    nws = cp.step_workspace_bytes(desc)
     wsb = torch.empty(nws + 2 * PAD * 4, dtype=torch.uint8, device="cuda")
     wsb.fill_(0x7F)
     ws = wsb[PAD * 4:PAD * 4 + nws]
+    ws[:cp.STEP_COUNTER_BYTES].zero_()  # the whole step's counters start at zero
     cp.attn_partial(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], o_part, lse_part,
                     workspace=ws, chunk_tokens=chunk)
     cp.lse_merge(o_part, lse_part, out, lse_out)
@@ -62,3 +63,4 @@ def test_outputs_stay_in_bounds(name, w, chunk):
     for k, b in bufs.items():
         assert untouched(b, torch.float32 if k != "out" else dt), f"{k} guard overwritten"
     assert bool((wsb[:PAD * 4] == 0x7F).all()) and bool((wsb[-PAD * 4:] == 0x7F).all())
+    assert int(torch.count_nonzero(ws[:cp.STEP_COUNTER_BYTES]).item()) == 0
