@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the context-parallel decode combine on one MI355X.
 
-One step = the whole hot path over one batch: cpdec_attn_partial (per-shard
-split-KV decode attention, including its in-kernel chunk merge) followed by
-cpdec_lse_merge (the cross-shard LSE merge).  The merge-only workload (c5)
-runs cpdec_lse_merge alone.  Inputs are synthetic, seeded, and resident in
-HBM before the timed region starts.
+One step = the whole hot path over one batch: per-shard split-KV decode
+attention, the merge of each shard's chunks and the cross-shard LSE merge.
+By default a step is one cpdec_cp_decode call (one kernel launch when the
+shape allows it); --two-calls times cpdec_attn_partial followed by
+cpdec_lse_merge instead.  The merge-only workload (c5) runs cpdec_lse_merge
+alone.  Inputs are synthetic, seeded, and resident in HBM before the timed
+region starts.
 
 Prints ONE JSON line:
   value          eager microseconds per call (wall clock of K back-to-back
                  steps launched from Python / K)
-  roofline       the dominant kernel (attention; the merge for c5):
-                 algorithmic bytes per launch / its mean duration from HIP
-                 events recorded around its launches on every 8th step of the
-                 timed region, against MI355X's 8 TB/s HBM peak (for split
-                 workloads the attention span includes its chunk-merge
-                 kernel); `traffic` is filled from the committed rocprofv3
+  roofline       the dominant kernel (the step's attention kernel, which
+                 also merges when the step is one launch; the merge kernel
+                 for c5): algorithmic bytes per launch / its mean duration
+                 from HIP events recorded around its launches on every 8th
+                 step of the timed region, against MI355X's 8 TB/s HBM peak
+                 (when the step takes several launches the span covers them
+                 all); `traffic` is filled from the committed rocprofv3
                  counter summary when it was taken on the current kernel
                  source, else null
   cpu_baseline   the CPU oracle timed on this host on a bounded sample of the
@@ -74,7 +77,7 @@ def merge_alg_bytes(R: int, rows: int, D: int, live: int, in_elem: int, out_elem
 
 
 # ------------------------------------------------------------------ GPU setup
-def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = False):
+def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = True):
     inp = sg.attn_inputs(w)
     lens = inp["lens_np"]
     per_copy = 2 * inp["k"].numel() * inp["k"].element_size()
@@ -92,7 +95,7 @@ def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = False):
     lse_out = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
     steps = []
     for s in sets:
-        if fused:  # cpdec_cp_decode: the whole step as one call (two launches)
+        if fused:  # cpdec_cp_decode: the whole step as one call
             a = cp.StepCall(s["q"], s["k_shards"], s["v_shards"], s["lens"], o_part, lse_part,
                             out, lse_out)
             m = None
@@ -105,7 +108,9 @@ def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = False):
     alg_merge = merge_alg_bytes(w.R, w.B * w.Hq, w.D, live_rows, 4, 2)
     info = dict(copies=copies, chunk=steps[0][0].plan["chunk_tokens"],
                 nchunks=steps[0][0].plan["num_chunks"], waves=steps[0][0].plan["waves"],
-                workspace_bytes=steps[0][0].workspace_bytes)
+                workspace_bytes=steps[0][0].workspace_bytes,
+                launches=(steps[0][0].launches if fused else
+                          (2 if steps[0][0].plan["num_chunks"] == 1 else 3)))
     return steps, alg_attn, alg_merge, info
 
 
@@ -214,9 +219,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--graph", action="store_true", help="also time HIP-graph replay of a step")
-    ap.add_argument("--fused", action="store_true",
-                    help="time the whole step as one cpdec_cp_decode call instead of "
-                         "cpdec_attn_partial + cpdec_lse_merge")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="time cpdec_attn_partial + cpdec_lse_merge instead of one "
+                         "cpdec_cp_decode call per step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy after the timed region (counter scaling)")
     args = ap.parse_args()
@@ -236,7 +241,8 @@ def main():
         steps, alg_attn, alg_merge, info = build_merge_steps(w, torch, cp, sg)
         K = args.steps or 100
     else:
-        steps, alg_attn, alg_merge, info = build_attn_steps(w, torch, cp, sg, fused=args.fused)
+        steps, alg_attn, alg_merge, info = build_attn_steps(w, torch, cp, sg,
+                                                            fused=not args.two_calls)
         K = args.steps or (200 if alg_attn < (1 << 30) else 20)
     W = args.warmup
     torch.cuda.synchronize()
@@ -282,15 +288,19 @@ def main():
     us_per_call = (t1 - t0) / K * 1e6
     attn_us = (float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])) * 1e3
                if not w.merge_only else None)
+    fused = not w.merge_only and not args.two_calls
     merge_us = (float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])) * 1e3
-                if not args.fused else None)
+                if not fused else None)
     device_us = edge[0].elapsed_time(edge[1]) * 1e3 / K
 
     if w.merge_only:
         dom_name, dom_us, dom_bytes, kernel = "lse_merge_kernel", merge_us, alg_merge, "lse_merge"
-    elif args.fused:  # the event span covers the whole step (attention + fused merge)
-        dom_name, dom_us, dom_bytes, kernel = ("attn_partial_kernel + attn_combine_merge_kernel",
-                                               attn_us, alg_attn + alg_merge, "attn_partial")
+    elif fused:  # the event span covers the whole step
+        rows = w.B * w.Hq
+        step_bytes = alg_attn + rows * (w.D * 2 + 4)  # + out and lse_out written once
+        dom_name = ("attn_partial_kernel (whole step, one launch)" if info["launches"] == 1 else
+                    f"cpdec_cp_decode ({info['launches']} launches)")
+        dom_us, dom_bytes, kernel = attn_us, step_bytes, "attn_partial"
     else:
         dom_name, dom_us, dom_bytes, kernel = "attn_partial_kernel", attn_us, alg_attn, "attn_partial"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -334,7 +344,9 @@ def main():
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_budget_s)
 
-    step_bytes = alg_attn + alg_merge
+    # algorithmic bytes of the whole step: the two-call form also writes and
+    # re-reads o_part between its calls
+    step_bytes = dom_bytes if fused else alg_attn + alg_merge
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 3),
@@ -348,14 +360,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f16",
         "data": "synthetic (seeded Philox streams; no dataset)",
-        "config": {"workload": f"{w.name}: {w.note}", "entry": ("cpdec_cp_decode" if args.fused else
-                                                          "cpdec_attn_partial + cpdec_lse_merge"),
+        "config": {"workload": f"{w.name}: {w.note}",
+                   "entry": ("cpdec_lse_merge" if w.merge_only else
+                             "cpdec_cp_decode" if fused else "cpdec_attn_partial + cpdec_lse_merge"),
+                   "launches_per_step": info.get("launches", 1),
                    "R": w.R, "B": w.B or None,
                    "Hq": w.Hq or None, "Hkv": w.Hkv or None, "D": w.D,
                    "rows": w.rows or None, "input_copies": info["copies"],
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
                    "waves_per_workgroup": info.get("waves"), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or args.fused
+        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or fused
                                                            or info.get("nchunks", 1) == 1
                                                            else " + attn_combine_kernel"),
                      "achieved": round(achieved, 1),

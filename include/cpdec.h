@@ -202,12 +202,14 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  * arrival counter per (sequence, kv head); the last workgroup of each such
  * group combines its shards' chunks, writes o_part/lse_part and merges the
  * shards.  The result does not depend on which workgroup arrives last.
- * Limits of the one-launch form: (sequences x kv heads x ceil(G/16)) <= 16384,
- * o_part below 2 GiB and, when shards are split into chunks, shards x chunks x
- * min(G,16) <= 2048 and shards x min(G,16) x D/4 <= 2048; beyond them the
- * step runs as attention, chunk-merge and merge launches (cpdec_step_plan
- * tells which).  `out` agrees with cpdec_lse_merge of the same partials to
- * rounding.
+ * The one-launch form needs a group that one workgroup can merge with one
+ * round of loads: groups (sequences x kv heads x ceil(G/16)) <= 1024, o_part
+ * below 2 GiB, and either unsplit shards (at most 8 shards, min(G,16) x D/4
+ * <= the workgroup's threads, at most 1024 workgroups) or split shards (at
+ * most 16 chunks, shards x min(G,16) x D/4 <= the workgroup's threads);
+ * otherwise the step runs as attention, chunk-merge and merge launches, where
+ * the merge work spreads over many workgroups (cpdec_step_plan tells which).
+ * `out` agrees with cpdec_lse_merge of the same partials to rounding.
  *
  *   d, q, k_shards, v_shards, lens, o_part, lse_part, stream
  *              as for cpdec_attn_partial

@@ -346,8 +346,12 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
     // ---- online softmax for head g = l16 ----
     float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                      fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    {  // over the 4 lane rows (q4) holding head g's tokens
+      const f32x2 a = rows16(mt);
+      mt = fmaxf(a[0], a[1]);
+      const f32x2 c = rows32(mt);
+      mt = fmaxf(c[0], c[1]);
+    }
     const float m_new = fmaxf(m, mt);  // finite: the tile holds >= 1 live token
     const float alpha = exp2f(m - m_new);
     // rescale the accumulators only when some head's running max grew
@@ -394,8 +398,12 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
       for (int j = 0; j < 8; ++j) vr[nb][j] = vrn[nb][j];
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  {
+    const f32x2 a = rows16(lsum);
+    lsum = a[0] + a[1];
+    const f32x2 c = rows32(lsum);
+    lsum = c[0] + c[1];
+  }
 
   // ---- merge the waves' states (wave 0 ends up holding the chunk result) ----
   if constexpr (NW > 1) {
@@ -668,6 +676,22 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
     return (uint32_t)(((slot00 + r * ustride * nch) * p.Gb + e / Q) * D * 4) + 16u * (e % Q);
   };
 
+  // ---- one round of loads: the chunk lse of this thread's (shard, head) pair
+  //      first (phase (1) waits only for those), then the first batch of its
+  //      first item's chunk vectors ----
+  constexpr int LB = 16;  // chunk lse values held in registers
+  const int pi0 = t;      // this thread's (shard, head) pair, if any
+  const int r0p = min(pi0 / ng, R - 1), g0p = pi0 - (pi0 / ng) * ng;
+  const int nl0p = pi0 < R * ng ? s_nl[r0p] : 0;
+  const uint32_t lstride = (uint32_t)(p.Gb * 4);
+  const uint32_t lbase0 = (uint32_t)(((slot00 + r0p * ustride * nch) * p.Gb + g0p) * 4);
+  float v0[LB];
+#pragma unroll
+  for (int j = 0; j < LB; ++j)
+    v0[j] = ld4f_dev(wl_rs, (nl0p >= 2 && j < nl0p) ? lbase0 + j * lstride : kOutOfRange);
+  const float l_one0 =
+      ld4f_dev(l_rs, nl0p == 1 ? (uint32_t)((r0p * rstride + row0 + g0p) * 4) : kOutOfRange);
+
   // ---- prefetch the first batch of this thread's first item ----
   const int it_first = t % per;
   const int r_first = min(it_first / E, R - 1), e_first = it_first % E;
@@ -693,17 +717,21 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
   for (int pi = t; pi < R * ng; pi += NT) {
     const int r = pi / ng, g = pi - r * ng;
     const int nl = s_nl[r];
+    const bool first = pi == pi0;
     float l = neg_inf();
     if (nl == 1) {
-      l = ld4f_dev(l_rs, (uint32_t)((r * rstride + row0 + g) * 4));
+      l = first ? l_one0 : ld4f_dev(l_rs, (uint32_t)((r * rstride + row0 + g) * 4));
     } else if (nl >= 2) {
       float* wr = ms.w + pi * nch;
       const uint32_t lbase = (uint32_t)(((slot00 + r * ustride * nch) * p.Gb + g) * 4);
-      const uint32_t lstride = (uint32_t)(p.Gb * 4);
-      constexpr int LB = 16;  // chunks held in registers
       float v[LB];
+      if (first) {
 #pragma unroll
-      for (int j = 0; j < LB; ++j) v[j] = ld4f_dev(wl_rs, j < nl ? lbase + j * lstride : kOutOfRange);
+        for (int j = 0; j < LB; ++j) v[j] = v0[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < LB; ++j) v[j] = ld4f_dev(wl_rs, j < nl ? lbase + j * lstride : kOutOfRange);
+      }
       float M = neg_inf();
       float S = 0.f;
       if (nl <= LB) {  // all in registers
@@ -807,6 +835,126 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
     merge_vector<D>(p, row0, e, R, ng, ms, [&](int r) { return ms.y[r * E + e]; });
 }
 
+// Merge of a split group with one query head (G == 1) whose (shard, chunk)
+// pairs fit one wave: lanes of wave 0 hold one chunk lse each (shard r in
+// lanes [r * nchp, (r + 1) * nchp), nchp = chunks rounded up to a power of
+// two), so every statistic is an xor-shuffle reduction; threads
+// (partition, shard, float4) sum their chunk vectors from registers.  Same
+// formulas as merge_chunks (chunk max, weights, shard lse; FP64 cross-shard
+// weights and lse), with the shuffle trees' summation order.
+template <int D, int NW>
+__device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
+                                MergeSmem<NW, kStepOneChunks>& ms, int lg_nchp) {
+  constexpr int NT = NW * 64;
+  constexpr int Q = D / 4;
+  constexpr int LGQ = __builtin_ctz(Q);
+  constexpr int KB = 16;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int R = p.R;
+  const int nch = p.nchunks;
+  const int nchp = 1 << lg_nchp;
+  const uint32_t es = esize(p.odt);
+  const int64_t nslots = (int64_t)p.units * nch;  // Gb == 1
+  const rsrc_t o_rs = make_rsrc(p.o_part, (uint32_t)((int64_t)R * p.B * p.Hq * D * es));
+  const rsrc_t l_rs = make_rsrc(p.lse_part, (uint32_t)((int64_t)R * p.B * p.Hq * 4));
+  const rsrc_t wo_rs = make_rsrc(p.ws_o, (uint32_t)(nslots * D * 4));
+  const rsrc_t wl_rs = make_rsrc(p.ws_lse, (uint32_t)(nslots * 4));
+  const int row0 = b * p.Hq + h;             // G == 1: query head h
+  const int rstride = p.B * p.Hq;            // o_part rows from shard to shard
+  const int sstride = p.B * p.Hkv * nch;     // workspace slots from shard to shard
+  const int slot00 = (b * p.Hkv + h) * nch;  // shard 0, chunk 0
+
+  // items (shard, float4): per = power of two >= R * Q threads, P partitions
+  int lg_per = LGQ;
+  while ((1 << lg_per) < R * Q) ++lg_per;
+  const int per = 1 << lg_per;
+  const int P = NT >> lg_per;
+  const int it = t & (per - 1), part = t >> lg_per;
+  const int ri = it >> LGQ, qi = it & (Q - 1);
+  const int nli = ri < R ? s_nl[ri] : 0;
+
+  // ---- one round of loads: wave 0's chunk lse first, then the chunk vectors ----
+  const int rl = lane >> lg_nchp, cl = lane & (nchp - 1);
+  const int nll = rl < R ? s_nl[rl] : 0;
+  const bool chunk_l = t < 64 && nll >= 2 && cl < nll;  // a live chunk of a split shard
+  const bool shard_l = t < 64 && nll == 1 && cl == 0;   // a shard with one live chunk
+  const float lc = ld4f_dev(wl_rs, chunk_l ? (uint32_t)((slot00 + rl * sstride + cl) * 4) : kOutOfRange);
+  const float ls1 = ld4f_dev(l_rs, shard_l ? (uint32_t)((rl * rstride + row0) * 4) : kOutOfRange);
+  f32x4 v[KB];
+  {
+    const uint32_t base = (uint32_t)((slot00 + ri * sstride) * D * 4) + 16u * qi;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int cc = part + j * P;
+      v[j] = __builtin_bit_cast(
+          f32x4, ld16_dev(wo_rs, (nli >= 2 && cc < nli) ? base + (uint32_t)cc * (D * 4) : kOutOfRange));
+    }
+  }
+  const f32x4 v_one = load4_dev(
+      o_rs, (nli == 1 && part == 0) ? (uint32_t)(((ri * rstride + row0) * D + 4 * qi) * es) : kOutOfRange,
+      p.odt);
+
+  // ---- (1)+(2) wave 0: chunk weights, shard lse, cross-shard weights ----
+  if (t < 64) {
+    const float lv = chunk_l ? lc : shard_l ? ls1 : neg_inf();
+    const float M = lane_reduce(lv, lg_nchp, OpMax{});     // over the shard's lanes
+    const float e = M == neg_inf() ? 0.f : expf(lv - M);  // -inf chunks give 0
+    const float S = lane_reduce(e, lg_nchp, OpSum{});
+    if (nll >= 2 && cl < nll) ms.w[rl * nch + cl] = e * (1.0f / S);
+    const float ls = S > 0.f ? M + logf(S) : neg_inf();  // shard lse (nl == 1: the stored one)
+    if (nll >= 2 && cl == 0) p.lse_part[rl * rstride + row0] = ls;
+    const float Mx = wave_max(cl == 0 ? ls : neg_inf());  // max over shards
+    const double ew = (cl == 0 && rl < R && ls != neg_inf()) ? exp((double)ls - (double)Mx) : 0.0;
+    const double St = wave_sum_f64(ew);
+    if (cl == 0 && rl < R) ms.lse[rl] = (float)ew;  // shard weight (unnormalised)
+    if (lane == 0) {
+      ms.M[0] = St > 0.0 ? (float)(1.0 / St) : 0.f;
+      if (p.lse_out != nullptr) p.lse_out[row0] = St > 0.0 ? (float)((double)Mx + log(St)) : neg_inf();
+    }
+  }
+  __syncthreads();
+
+  // ---- (3) shard vectors ----
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  if (ri < R) {
+    if (nli >= 2) {
+      const float* wr = ms.w + ri * nch;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int cc = part + j * P;
+        if (cc < nli) y += wr[cc] * v[j];
+      }
+    } else if (nli == 1) {
+      y = v_one;
+    }
+  }
+  if (P > 1) {
+    ms.part[t] = y;
+    __syncthreads();
+    if (part == 0)
+      for (int q = 1; q < P; ++q) y += ms.part[t + q * per];
+  }
+  if (part == 0 && ri < R) {
+    if (nli >= 2) {
+      store4(p.o_part, (int64_t)(ri * rstride + row0) * D + 4 * qi, y, p.odt);
+      y = round4(y, p.odt);
+    }
+    ms.y[it] = y;
+  }
+  __syncthreads();
+
+  // ---- (4) cross-shard merge, shard order ----
+  if (t < Q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r) {
+      const float w = ms.lse[r];
+      if (w != 0.f) acc += w * ms.y[r * Q + t];
+    }
+    store4(p.out, (int64_t)row0 * D + 4 * t, acc * ms.M[0], p.out_dt);
+  }
+}
+
 template <typename T, int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
   const Args p = load_args(kp);
@@ -863,10 +1011,16 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     }
     __syncthreads();
     if (!s_last) return;
-    if constexpr (MODE == kStepOneShards)
+    if constexpr (MODE == kStepOneShards) {
       merge_shards<D, NW>(p, b, h, gb, s_nl, sh.m);
-    else
-      merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
+    } else {
+      int lg_nchp = 0;
+      while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
+      if (p.G == 1 && (p.R << lg_nchp) <= 64)
+        merge_chunks_g1<D, NW>(p, b, h, s_nl, sh.m, lg_nchp);
+      else
+        merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
+    }
   }
 }
 
@@ -901,16 +1055,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) 
   for (int g = wave; g < ng; g += 4) {
     float M = neg_inf();
     for (int cc = lane; cc < nlive; cc += 64) M = fmaxf(M, p.ws_lse[(slot0 + cc) * p.Gb + g]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    M = wave_max(M);
     float S = 0.f;
     for (int cc = lane; cc < nlive; cc += 64) {
       const float e = expf(p.ws_lse[(slot0 + cc) * p.Gb + g] - M);
       w[cc][g] = e;
       S += e;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+    S = wave_sum(S);
     const float invS = 1.0f / S;
     for (int cc = lane; cc < nlive; cc += 64) w[cc][g] *= invS;
     if (lane == 0) p.lse_part[orow0 + g] = M + logf(S);

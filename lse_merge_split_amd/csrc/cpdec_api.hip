@@ -109,6 +109,15 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
     chunk = (int)ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
   p.chunk = chunk;
   p.nchunks = (int)ceil_div(cap, chunk);
+  // Split shards: the workgroup that merges a group in the one-launch step
+  // needs a thread per (shard, head, float4) item; give it more waves when
+  // that lets the group fit (a wave past the chunk's end simply sees no tile).
+  if (!overrides().waves && p.nchunks > 1) {
+    const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
+    int w = p.waves;
+    while (w < 8 && items > 64 * w) w *= 2;
+    if (items <= 64 * w) p.waves = w;
+  }
 
   const int64_t blocks = p.units * p.nchunks;
   if (blocks > INT32_MAX || p.units > INT32_MAX ||
@@ -131,13 +140,18 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   const int64_t groups = (int64_t)d->batch * d->num_kv_heads * p.gblocks;
   const uint64_t opart_bytes = (uint64_t)d->num_shards * d->batch * d->num_q_heads * D *
                                (d->opart_dtype == CPDEC_F32 ? 4u : 2u);
+  const int64_t threads = 64 * p.waves;
+  const int64_t R = d->num_shards;
   bool one = !overrides().step_launches && groups <= kStepCounters && opart_bytes < (1ull << 31);
-  if (p.nchunks > 1)
-    one = one && (int64_t)d->num_shards * p.nchunks * p.Gb <= kStepSlots &&
-          (int64_t)d->num_shards * p.Gb * (D / 4) <= kStepVecs &&
+  if (p.nchunks > 1) {
+    const int64_t items = R * p.Gb * (D / 4);
+    one = one && items <= threads && items <= kStepVecs && R * p.Gb <= threads &&
+          p.nchunks <= kStepMaxChunks && R * p.nchunks * p.Gb <= kStepSlots &&
           slots * (size_t)D * sizeof(float) < (1ull << 31);
-  else  // large unsplit grids: a merge launch costs less than write-through o_part stores
-    one = one && p.units <= kStepUnsplitBlocks;
+  } else {  // large unsplit grids: a merge launch costs less than write-through o_part stores
+    one = one && p.units <= kStepUnsplitBlocks && R <= kStepMaxShardsUnsplit &&
+          (int64_t)p.Gb * (D / 4) <= threads;
+  }
   p.step = !one ? kStepLaunches : (p.nchunks > 1 ? kStepOneChunks : kStepOneShards);
   *pl = p;
   return CPDEC_OK;

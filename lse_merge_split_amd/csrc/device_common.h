@@ -110,6 +110,81 @@ __device__ __forceinline__ float buf4f(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// ---- lane exchanges in VALU (no LDS crossbar) ------------------------------
+// DPP within a 16-lane row: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at
+// distance 1 and 2, the half-row mirror pairs lane i with 7-i and the row
+// mirror lane i with 15-i; gfx950's permlane16/32 swaps exchange rows.  A
+// butterfly of these over a commutative operation leaves the identical
+// result in every lane of the group (each step pairs lanes symmetrically).
+// Every lane of the wave must be active.
+enum LaneStep : int { kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140 };
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// The two values that rows r and r ^ 1 (xor 16) or halves (xor 32) hold.
+__device__ __forceinline__ f32x2 rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+__device__ __forceinline__ f32x2 rows32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
+// Reduce over aligned groups of 2^levels lanes (levels 0..6).
+template <typename Op>
+__device__ __forceinline__ float lane_reduce(float x, int levels, Op op) {
+  if (levels > 0) x = op(x, dpp<kXor1>(x));
+  if (levels > 1) x = op(x, dpp<kXor2>(x));
+  if (levels > 2) x = op(x, dpp<kHalfMirror>(x));
+  if (levels > 3) x = op(x, dpp<kMirror>(x));
+  if (levels > 4) { const f32x2 r = rows16(x); x = op(r[0], r[1]); }
+  if (levels > 5) { const f32x2 r = rows32(x); x = op(r[0], r[1]); }
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) { return lane_reduce(x, 6, OpMax{}); }
+__device__ __forceinline__ float wave_sum(float x) { return lane_reduce(x, 6, OpSum{}); }
+// FP64 sum over the wave (halves exchanged separately).
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  auto ex = [](double v, auto f) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const float lo = f(__builtin_bit_cast(float, (uint32_t)u));
+    const float hi = f(__builtin_bit_cast(float, (uint32_t)(u >> 32)));
+    return __builtin_bit_cast(double, (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                                          ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32));
+  };
+  x += ex(x, [](float v) { return dpp<kXor1>(v); });
+  x += ex(x, [](float v) { return dpp<kXor2>(v); });
+  x += ex(x, [](float v) { return dpp<kHalfMirror>(v); });
+  x += ex(x, [](float v) { return dpp<kMirror>(v); });
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const f32x2 lo = rows16(__builtin_bit_cast(float, (uint32_t)u));
+    const f32x2 hi = rows16(__builtin_bit_cast(float, (uint32_t)(u >> 32)));
+    auto mk = [](float l, float h) {
+      return __builtin_bit_cast(double, (uint64_t)__builtin_bit_cast(uint32_t, l) |
+                                            ((uint64_t)__builtin_bit_cast(uint32_t, h) << 32));
+    };
+    x = mk(lo[0], hi[0]) + mk(lo[1], hi[1]);
+  }
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const f32x2 lo = rows32(__builtin_bit_cast(float, (uint32_t)u));
+    const f32x2 hi = rows32(__builtin_bit_cast(float, (uint32_t)(u >> 32)));
+    auto mk = [](float l, float h) {
+      return __builtin_bit_cast(double, (uint64_t)__builtin_bit_cast(uint32_t, l) |
+                                            ((uint64_t)__builtin_bit_cast(uint32_t, h) << 32));
+    };
+    x = mk(lo[0], hi[0]) + mk(lo[1], hi[1]);
+  }
+  return x;
+}
+
 // ---- hand-off between workgroups of one launch ---------------------------
 // Cache-policy bit sc1 (device scope).  A device-scope store is written
 // through to the level that every XCD's device-scope loads read, and a

@@ -43,13 +43,20 @@ enum StepMode : int {
                        // the last chunk workgroup combines chunks and merges
 };
 
-// Limits of the one-launch step (the merging workgroup's LDS and counters).
+// Limits of the one-launch step.  The workgroup that merges a group fetches
+// everything it needs in one round of loads, so the group must fit it: at
+// most one (shard, head) pair and one (shard, head, float4) item per thread,
+// at most 16 chunks per shard (16 loads per thread), at most 8 shards when
+// shards are not split.  Larger groups take separate launches, where the
+// merge work spreads over many workgroups.
 constexpr size_t kStepCounterBytes = 65536; // counters at the start of the workspace
 constexpr int kStepCounterStride = 16;      // ints: one 64-byte line per counter (atomics
                                             // on one line serialise across groups)
 constexpr int kStepCounters = (int)(kStepCounterBytes / 4 / kStepCounterStride);  // groups
+constexpr int kStepMaxChunks = 16;          // chunks per shard, split shards
+constexpr int kStepMaxShardsUnsplit = 8;    // shards, unsplit
 constexpr int kStepSlots = 2048;            // shards * chunks * heads of one group
-constexpr int kStepVecs = 2048;             // shards * heads * D/4 of one group
+constexpr int kStepVecs = 512;              // shards * heads * D/4 of one group (<= threads)
 constexpr int64_t kStepUnsplitBlocks = 1024; // unsplit shards: one launch up to this grid
 
 // Launch the partial-attention kernel over units x nchunks workgroups and

@@ -66,11 +66,15 @@ def test_workspace_bytes():
 def test_step_plan_launches():
     assert cp.step_launches(_desc(chunk_tokens=1024)) == 1     # shards merged in the launch
     assert cp.step_launches(_desc(chunk_tokens=128)) == 1      # chunks and shards in the launch
-    # 4 shards x 16 heads x 256/4 vectors exceed the merging workgroup's LDS
+    # 16 heads x 256/4 vectors per shard: more than one merging workgroup's threads
     wide = dict(num_q_heads=32, num_kv_heads=2, head_dim=256, kv_stride_token=256,
                 kv_stride_head=1000 * 256, kv_stride_batch=2 * 1000 * 256)
     assert cp.step_launches(_desc(chunk_tokens=128, **wide)) == 3  # attention, combine, merge
-    assert cp.step_launches(_desc(chunk_tokens=1024, **wide)) == 1
+    assert cp.step_launches(_desc(chunk_tokens=1024, **wide)) == 2  # attention, merge
+    # more than 16 chunks per shard
+    assert cp.step_launches(_desc(chunk_tokens=32)) == 3
+    # more than 8 whole shards
+    assert cp.step_launches(_desc(chunk_tokens=1024, num_shards=9)) == 2
     # more (sequence, kv head) groups than counters
     many = dict(batch=8193, kv_stride_batch=2 * 1000 * 128)
     assert cp.step_launches(_desc(chunk_tokens=1024, **many)) == 2  # attention, merge

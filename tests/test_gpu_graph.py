@@ -18,8 +18,8 @@ from synth import gpu as sg  # noqa: E402
     ("split shards (chunk merge)", sc.small("c4", B=8, Lcap=700)),
     ("whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
     ("merge-only rows", None),
-    ("one-launch step, split", sc.small("c4", B=2, Lcap=700)),
-    ("one-launch step, whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
+    ("one-launch step, split", sc.small("c4", B=2, Hq=8, Lcap=700)),
+    ("one-launch step, whole shards", sc.small("c3", B=8, Lcap=640, L=600)),
 ])
 def test_graph_replay_matches_eager(name, w):
     print(f"[case] graph replay: {name}", flush=True)

@@ -28,12 +28,13 @@ CASES = {
     "c1": (sc.WORKLOADS["c1"], 0, 1),
     "c1 chunk 32": (sc.WORKLOADS["c1"], 32, 1),
     "c2": (sc.WORKLOADS["c2"], 0, 1),
-    "c2 chunk 32 (128 chunks)": (sc.WORKLOADS["c2"], 32, 1),
+    "c2 chunk 32 (128 chunks: separate launches)": (sc.WORKLOADS["c2"], 32, 3),
     "ragged GQA 8, B16": (sc.small("c4", B=16, Lcap=512), 0, 1),
-    "ragged GQA 8, B2 split": (sc.small("c4", B=2, Lcap=512), 0, 1),
+    "ragged GQA 8, B2 split (group too big: separate launches)": (sc.small("c4", B=2, Lcap=512), 0, 3),
     "ragged GQA 8, B64 (large unsplit grid)": (sc.small("c4", B=64, Lcap=512), 0, 2),
     "D256 G20 (over the LDS limit)": (sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290), 0, 3),
-    "fp16 GQA 8 split": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 1),
+    "fp16 GQA 8 split (separate launches)": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 3),
+    "fp16 GQA 2 split": (sc.small("c4", B=2, Hq=16, Lcap=256, dtype="fp16"), 0, 1),
     "D64 G3": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 0, 1),
     "D64 G3 chunk 32": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 32, 1),
     "D256 G2 split": (sc.small("c3", R=2, B=1, Hq=4, Hkv=2, D=256, Lcap=700, L=650), 0, 1),
@@ -182,7 +183,8 @@ def test_step_16bit_partials(o_dt):
     """o_part stored in 16 bits: the merged output meets the bar against the
     storage-aware oracle (exact partials rounded to the storage type, then
     merged exactly), on the one-launch split and unsplit forms."""
-    for name, w in (("split", sc.small("c4", B=2, Lcap=512)), ("unsplit", sc.small("c4", B=16, Lcap=512))):
+    for name, w in (("split", sc.small("c4", B=2, Hq=16, Lcap=512)),
+                    ("unsplit", sc.small("c4", B=16, Lcap=512))):
         _say(f"step 16-bit partials {o_dt} {name}")
         inp = sg.attn_inputs(w)
         ws, desc = step_workspace(inp)
