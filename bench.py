@@ -257,12 +257,12 @@ def main():
             if ev is not None:
                 ev[0].record()
             a(stream)
-        if ev is not None:
+        if ev is not None and (m is not None or a is not None):
             ev[1].record()
         if m is not None:
             m(stream)
-        if ev is not None:
-            ev[2].record()
+            if ev is not None:
+                ev[2].record()
 
     for i in range(W):
         step(i)
@@ -270,8 +270,9 @@ def main():
 
     # HIP events bracket the kernels of every EVERY-th timed step (each event
     # record costs a few microseconds of device time, so bracketing every step
-    # would inflate the per-step time of the small workloads).
-    EVERY = 8
+    # would inflate the per-step time of the small workloads; a one-call step
+    # takes two events).
+    EVERY = 16
     sampled = list(range(0, K, EVERY))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

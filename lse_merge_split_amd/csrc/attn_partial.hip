@@ -195,55 +195,52 @@ struct Args {
   float* lse_out;
   int32_t* counters;
   int64_t sb, sh, st;
-  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt, out_dt;
+  int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt, out_dt, cap;
   float scale_log2;
 };
 
 // (readfirstlane afterwards: the compiler takes an asm result for a per-lane
 // value, and a buffer resource built from one would need a waterfall loop.)
-__device__ __forceinline__ uint32_t opaque32(uint32_t x) {
-  asm volatile("" : "+s"(x));
-  return __builtin_amdgcn_readfirstlane(x);
-}
+// All fields pass through ONE asm statement, so every argument load is issued
+// before the first wait (one memory round trip instead of one per field).
+__device__ __forceinline__ uint32_t rfl(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 template <typename V>
-__device__ __forceinline__ V opaque(V x) {
-  static_assert(sizeof(V) == 4 || sizeof(V) == 8, "32- or 64-bit values");
+__device__ __forceinline__ V rfl_v(V x) {
   if constexpr (sizeof(V) == 4) {
-    return __builtin_bit_cast(V, opaque32(__builtin_bit_cast(uint32_t, x)));
+    return __builtin_bit_cast(V, rfl(__builtin_bit_cast(uint32_t, x)));
   } else {
     const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint64_t lo = opaque32((uint32_t)u), hi = opaque32((uint32_t)(u >> 32));
-    return __builtin_bit_cast(V, lo | (hi << 32));
+    return __builtin_bit_cast(V, (uint64_t)rfl((uint32_t)u) | ((uint64_t)rfl((uint32_t)(u >> 32)) << 32));
   }
 }
 
-__device__ __forceinline__ Args load_args(const AttnParams& p) {
+__device__ __forceinline__ Args load_args(const AttnParams& p, const void*& kshard,
+                                          const void*& vshard) {
   Args a;
-  a.q = opaque(p.q);
-  a.lens = opaque(p.lens);
-  a.o_part = opaque(p.o_part);
-  a.lse_part = opaque(p.lse_part);
-  a.ws_o = opaque(p.ws_o);
-  a.ws_lse = opaque(p.ws_lse);
-  a.out = opaque(p.out);
-  a.lse_out = opaque(p.lse_out);
-  a.counters = opaque(p.counters);
-  a.sb = opaque(p.sb);
-  a.sh = opaque(p.sh);
-  a.st = opaque(p.st);
-  a.B = opaque(p.B);
-  a.Hq = opaque(p.Hq);
-  a.Hkv = opaque(p.Hkv);
-  a.G = opaque(p.G);
-  a.Gb = opaque(p.Gb);
-  a.gblocks = opaque(p.gblocks);
-  a.R = opaque(p.R);
-  a.chunk = opaque(p.chunk);
-  a.nchunks = opaque(p.nchunks);
-  a.units = opaque(p.units);
-  a.odt = opaque(p.odt);
-  a.out_dt = opaque(p.out_dt);
-  a.scale_log2 = opaque(p.scale_log2);
+  a.q = p.q; a.lens = p.lens; a.o_part = p.o_part; a.lse_part = p.lse_part; a.ws_o = p.ws_o;
+  a.ws_lse = p.ws_lse; a.out = p.out; a.lse_out = p.lse_out; a.counters = p.counters;
+  a.sb = p.sb; a.sh = p.sh; a.st = p.st;
+  a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.Gb = p.Gb; a.gblocks = p.gblocks; a.R = p.R;
+  a.chunk = p.chunk; a.nchunks = p.nchunks; a.units = p.units; a.odt = p.odt; a.out_dt = p.out_dt;
+  a.cap = p.cap; a.scale_log2 = p.scale_log2;
+  kshard = p.k[blockIdx.y];
+  vshard = p.v[blockIdx.y];
+  asm volatile(""
+               : "+s"(a.q), "+s"(a.lens), "+s"(a.o_part), "+s"(a.lse_part), "+s"(a.ws_o),
+                 "+s"(a.ws_lse), "+s"(a.out), "+s"(a.lse_out), "+s"(a.counters), "+s"(a.sb),
+                 "+s"(a.sh), "+s"(a.st), "+s"(kshard), "+s"(vshard), "+s"(a.B), "+s"(a.Hq),
+                 "+s"(a.Hkv), "+s"(a.G), "+s"(a.Gb), "+s"(a.gblocks), "+s"(a.R), "+s"(a.chunk),
+                 "+s"(a.nchunks), "+s"(a.units), "+s"(a.odt), "+s"(a.out_dt), "+s"(a.cap),
+                 "+s"(a.scale_log2));
+  a.q = rfl_v(a.q); a.lens = rfl_v(a.lens); a.o_part = rfl_v(a.o_part);
+  a.lse_part = rfl_v(a.lse_part); a.ws_o = rfl_v(a.ws_o); a.ws_lse = rfl_v(a.ws_lse);
+  a.out = rfl_v(a.out); a.lse_out = rfl_v(a.lse_out); a.counters = rfl_v(a.counters);
+  a.sb = rfl_v(a.sb); a.sh = rfl_v(a.sh); a.st = rfl_v(a.st);
+  kshard = rfl_v(kshard); vshard = rfl_v(vshard);
+  a.B = rfl_v(a.B); a.Hq = rfl_v(a.Hq); a.Hkv = rfl_v(a.Hkv); a.G = rfl_v(a.G); a.Gb = rfl_v(a.Gb);
+  a.gblocks = rfl_v(a.gblocks); a.R = rfl_v(a.R); a.chunk = rfl_v(a.chunk);
+  a.nchunks = rfl_v(a.nchunks); a.units = rfl_v(a.units); a.odt = rfl_v(a.odt);
+  a.out_dt = rfl_v(a.out_dt); a.cap = rfl_v(a.cap); a.scale_log2 = rfl_v(a.scale_log2);
   return a;
 }
 
@@ -252,9 +249,9 @@ __device__ __forceinline__ Args load_args(const AttnParams& p) {
 // chunk, else to the workspace.  In the one-launch step modes these stores are
 // device-scope, for the workgroup that merges the group.
 template <typename T, int D, int NW, int MODE>
-__device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, const void* vshard,
+__device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, const void* vshard,
                                              Smem<D, NW>& sm, int c, int unit, int r, int b, int h,
-                                             int gb, int L) {
+                                             int gb, int len_raw, int& len_t) {
   constexpr int NCH = D / 8;           // 16-byte chunks per token row
   constexpr int NB = (NCH + 15) / 16;  // 16-chunk row blocks of the PV product
   constexpr int KS = D / 32;           // k-steps of the QK product
@@ -270,15 +267,15 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
   const int ng = min(kGroupRows, p.G - g0);
   const int hq0 = h * p.G + g0;
   const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + hq0;  // o_part/lse_part row of head g0
-  const int t_end = min(L, t_begin + p.chunk);
-  const int nlive = (L + p.chunk - 1) / p.chunk;
 
   // Q operand (B of S^T = K Q^T): lane (q4, g = l16) holds Q[g][32 s + 8 q4 .. +8].
   u32x4 qop[KS];
   {
-    const T* qrow = static_cast<const T*>(p.q) + ((int64_t)b * p.Hq + hq0 + l16) * D + 8 * q4;
+    const rsrc_t qrs = make_rsrc(static_cast<const T*>(p.q) + ((int64_t)b * p.Hq + hq0) * D,
+                                 (uint32_t)(ng * D * sizeof(T)));  // the group's heads
+    const uint32_t qoff = (uint32_t)((l16 * D + 8 * q4) * sizeof(T));
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = (l16 < ng) ? ld16(qrow + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < KS; ++s) qop[s] = buf16(qrs, l16 < ng ? qoff + 64u * s : kOutOfRange);
   }
 
   const T* kb = static_cast<const T*>(kshard) + b * p.sb + h * p.sh;
@@ -299,11 +296,14 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
   // token: rows past it read as zeros without memory traffic, so the tail and
   // the prefetch beyond the end need neither clamping nor a branch (a branch
   // around loads makes the compiler drain every outstanding load at the join).
-  const uint32_t span = (uint32_t)(((int64_t)(t_end - 1) * st + D) * sizeof(T));
-  const rsrc_t krs = make_rsrc(kb, span);
-  const rsrc_t vrs = make_rsrc(vb, span);
+  // The wave's first tile is requested before the length is known, through a
+  // resource that ends at the chunk's end within the capacity; a tile that
+  // crosses the end zeroes its V rows past it before they are used.
   const uint32_t rowb = (uint32_t)(st * sizeof(T));  // bytes per token row
-  auto load_tile = [&](int t0, u32x4 (&kr)[2][KS], u32x4 (&vr)[NB][8]) {
+  auto rows_span = [&](int rows) {
+    return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * st + D) * sizeof(T)) : 0u;
+  };
+  auto load_tile = [&](int t0, rsrc_t krs, rsrc_t vrs, u32x4 (&kr)[2][KS], u32x4 (&vr)[NB][8]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const uint32_t off = (uint32_t)(t0 + 16 * blk + l16) * rowb + 16u * q4;
@@ -323,11 +323,29 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
 
   u32x4 kr[2][KS], vr[NB][8];
   int t0 = t_begin + wave * kTileTokens;
-  load_tile(t0, kr, vr);
-  for (; t0 < t_end; t0 += NW * kTileTokens) {
+  {
+    const uint32_t span0 = rows_span(min(p.cap, t_begin + p.chunk));
+    load_tile(t0, make_rsrc(kb, span0), make_rsrc(vb, span0), kr, vr);
+  }
+  if constexpr (kDev) {  // every shard's length of this sequence, for the merge (used at the end)
+    const rsrc_t lens_rs = make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4));
+    len_t = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        lens_rs, threadIdx.x < (unsigned)p.R ? (int)((threadIdx.x * p.B + b) * 4) : (int)kOutOfRange, 0,
+        0);
+  }
+  const int L = __builtin_amdgcn_readfirstlane(len_raw);
+  const int t_end = min(L, t_begin + p.chunk);  // <= t_begin for an empty chunk
+  const int nlive = (L + p.chunk - 1) / p.chunk;
+  const uint32_t span = rows_span(t_end);
+  const rsrc_t krs = make_rsrc(kb, span);
+  const rsrc_t vrs = make_rsrc(vb, span);
+  // The first tile is always processed (fully masked when the wave's part of
+  // the chunk is empty): no branch may separate its loads from their use, or
+  // the compiler moves the loads behind the length check.
+  do {
     // prefetch the wave's next tile while this one is computed
     u32x4 krn[2][KS], vrn[NB][8];
-    load_tile(t0 + NW * kTileTokens, krn, vrn);
+    load_tile(t0 + NW * kTileTokens, krs, vrs, krn, vrn);
 
     // ---- scores S^T (16 tokens x 16 heads per block), base-2 scaled, masked ----
     float x[2][4];
@@ -352,17 +370,30 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
       const f32x2 c = rows32(mt);
       mt = fmaxf(c[0], c[1]);
     }
-    const float m_new = fmaxf(m, mt);  // finite: the tile holds >= 1 live token
-    const float alpha = exp2f(m - m_new);
+    const float m_new = fmaxf(m, mt);  // -inf only while every token so far was masked
+    const float m_ref = m_new == neg_inf() ? 0.f : m_new;  // keeps -inf - -inf out
+    const float alpha = exp2f(m - m_ref);
     // rescale the accumulators only when some head's running max grew
     // (rare after the first tiles); the branch is wave-uniform and holds no loads
     const bool grew = __any(m_new > m);
     m = m_new;
     float pr[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_new);
+    for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_ref);
     float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     lsum = lsum * alpha + ps;
+
+    // A tile crossing the end: V rows past it (padding read by the first,
+    // speculative load) become zeros, since 0 * NaN would poison the sums.
+    if (t0 + kTileTokens > t_end) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool dead = t0 + tile_token(q4, j) >= t_end;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          if (dead) vr[nb][j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
 
     // P operand (B of O^T = V^T P^T), split into hi + lo 16-bit parts.
     u32x4 phi, plo;
@@ -396,7 +427,9 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) vr[nb][j] = vrn[nb][j];
-  }
+    t0 += NW * kTileTokens;
+  } while (t0 < t_end);
+  if (t_begin >= L) return false;  // empty chunk: nothing is written
 
   {
     const f32x2 a = rows16(lsum);
@@ -476,7 +509,7 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
           p.lse_part[orow0 + l16] = lse_nat;
       }
     }
-    return;
+    return true;
   }
 
   // ---- several live chunks: this chunk's normalised partial to the workspace ----
@@ -506,6 +539,7 @@ __device__ __forceinline__ void attend_chunk(const Args& p, const void* kshard, 
         p.ws_lse[slot * p.Gb + l16] = lse_nat;
     }
   }
+  return true;
 }
 
 // Cross-shard weights of one group, one thread per (shard r, head g) pair:
@@ -957,35 +991,35 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
 
 template <typename T, int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
-  const Args p = load_args(kp);
+  const void* kshard;
+  const void* vshard;
+  const Args p = load_args(kp, kshard, vshard);
   __shared__ KernelSmem<T, D, NW, MODE> sh;
   __shared__ int s_last;
   __shared__ int s_nl[MODE >= kStepOneShards ? kMaxShards : 1];  // live chunks per shard
 
-  // Chunk-major order: workgroups are dealt to the 8 XCDs round-robin by
-  // block index, so block % 8 must not correlate with the chunk index (the
-  // later chunks of ragged shards are mostly empty); here it follows the unit.
-  const int c = blockIdx.x / p.units;
-  const int unit = blockIdx.x % p.units;
-  int u = unit;
+  // Grid: x = (chunk, unit within the shard), chunk-major; y = shard.  The
+  // shard's K/V pointers are then fetched with the other arguments at once.
+  // Workgroups are dealt to the 8 XCDs round-robin by linear block index, so
+  // block % 8 must not correlate with the chunk index (the later chunks of
+  // ragged shards are mostly empty); here it follows the unit.
+  const int r = blockIdx.y;
+  const int upr = p.B * p.Hkv * p.gblocks;  // units per shard
+  const int c = blockIdx.x / upr;
+  const int uis = blockIdx.x - c * upr;
+  const int unit = r * upr + uis;
+  int u = uis;
   const int gb = u % p.gblocks; u /= p.gblocks;
-  const int h = u % p.Hkv; u /= p.Hkv;
-  const int b = u % p.B;
-  const int r = u / p.B;
-  const int L = __builtin_amdgcn_readfirstlane(p.lens[r * p.B + b]);  // uniform address
+  const int h = u % p.Hkv;
+  const int b = u / p.Hkv;
+  // this shard's length (waited for inside, after the first tile is requested)
+  const int len_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4)), (r * p.B + b) * 4, 0, 0);
   // One-launch step: every shard's length of this sequence, for whichever
-  // workgroup ends up merging (issued now, used after the attention).
+  // workgroup ends up merging (requested early inside, used after the attention).
   int len_t = 0;
-  if constexpr (MODE >= kStepOneShards) {
-    const rsrc_t lens_rs = make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4));
-    len_t = (int)__builtin_amdgcn_raw_buffer_load_b32(
-        lens_rs, threadIdx.x < (unsigned)p.R ? (int)((threadIdx.x * p.B + b) * 4) : (int)kOutOfRange, 0,
-        0);
-  }
-
-  if (c * p.chunk < L) {
-    attend_chunk<T, D, NW, MODE>(p, kp.k[r], kp.v[r], sh.a, c, unit, r, b, h, gb, L);
-  } else if (c == 0) {  // empty shard: o_r = 0, lse_r = -inf (the merge never reads them)
+  if (!attend_chunk<T, D, NW, MODE>(p, kshard, vshard, sh.a, c, unit, r, b, h, gb, len_raw, len_t) &&
+      c == 0) {  // empty shard: o_r = 0, lse_r = -inf (the merge never reads them)
     const int g0 = gb * kGroupRows;
     const int ng = min(kGroupRows, p.G - g0);
     const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
@@ -1032,7 +1066,9 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
 // (results do not depend on timing).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) {
-  const Args p = load_args(kp);
+  const void* ks_unused;
+  const void* vs_unused;
+  const Args p = load_args(kp, ks_unused, vs_unused);
   __shared__ float w[kMaxChunks][16];
   __shared__ f32x4 part[256];
   const int unit = blockIdx.x;
@@ -1101,7 +1137,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) 
 
 template <typename T, int D, int NW>
 hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipStream_t s) {
-  const dim3 grid((unsigned)(units * p.nchunks)), block(NW * 64);
+  const dim3 grid((unsigned)(units / p.R * p.nchunks), (unsigned)p.R), block(NW * 64);
   if (mode == kStepOneShards) {
     hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneShards>), grid, block, 0, s, p);
     return hipGetLastError();

@@ -287,6 +287,7 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
   p.chunk = pl.chunk;
   p.nchunks = pl.nchunks;
   p.units = (int32_t)pl.units;
+  p.cap = d->kv_capacity;
   p.odt = d->opart_dtype;
   const double scale = d->sm_scale > 0.f ? (double)d->sm_scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);

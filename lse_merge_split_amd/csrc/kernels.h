@@ -25,6 +25,7 @@ struct AttnParams {
   float* ws_lse;      // [units][nchunks][Gb]    chunk lse (natural log)
   int64_t sb, sh, st; // K/V element strides: batch, head, token
   int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt;
+  int32_t cap;        // K/V capacity per (shard, sequence, kv head), tokens
   float scale_log2;   // sm_scale * log2(e)
   // the whole step (cpdec_cp_decode) only:
   void* out;          // [B][Hq][D] merged output, dtype out_dt
@@ -59,7 +60,7 @@ constexpr int kStepSlots = 2048;            // shards * chunks * heads of one gr
 constexpr int kStepVecs = 512;              // shards * heads * D/4 of one group (<= threads)
 constexpr int64_t kStepUnsplitBlocks = 1024; // unsplit shards: one launch up to this grid
 
-// Launch the partial-attention kernel over units x nchunks workgroups and
+// Launch the partial-attention kernel over (units / R) x nchunks x R workgroups and
 // whatever else `mode` needs (chunk combine and merge kernels for
 // kPartialsOnly/kStepLaunches; nothing for the one-launch modes).
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
