@@ -109,8 +109,10 @@ def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = True):
     info = dict(copies=copies, chunk=steps[0][0].plan["chunk_tokens"],
                 nchunks=steps[0][0].plan["num_chunks"], waves=steps[0][0].plan["waves"],
                 workspace_bytes=steps[0][0].workspace_bytes,
+                longest_first=steps[0][0].plan["longest_first"],
                 launches=(steps[0][0].launches if fused else
-                          (2 if steps[0][0].plan["num_chunks"] == 1 else 3)))
+                          (2 if steps[0][0].plan["num_chunks"] == 1 else 3)
+                          + int(steps[0][0].plan["longest_first"])))
     return steps, alg_attn, alg_merge, info
 
 
@@ -369,10 +371,12 @@ def main():
                    "Hq": w.Hq or None, "Hkv": w.Hkv or None, "D": w.D,
                    "rows": w.rows or None, "input_copies": info["copies"],
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
-                   "waves_per_workgroup": info.get("waves"), "parallelism": "single GPU"},
+                   "waves_per_workgroup": info.get("waves"),
+                   "longest_first": info.get("longest_first"), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or fused
                                                            or info.get("nchunks", 1) == 1
-                                                           else " + attn_combine_kernel"),
+                                                           else " + attn_combine_kernel")
+                     + (" + order_kernel" if info.get("longest_first") else ""),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,

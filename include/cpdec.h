@@ -84,12 +84,15 @@ typedef struct cpdec_attn_desc {
 
 /*
  * Bytes of device workspace cpdec_attn_partial needs for `d` (0 when every
- * shard fits one chunk).  Returns 0 for an invalid descriptor as well; such a
- * descriptor is then rejected by cpdec_attn_partial itself.
+ * shard fits one chunk and the launch keeps index order).  Returns 0 for an
+ * invalid descriptor as well; such a descriptor is then rejected by
+ * cpdec_attn_partial itself.
  *
  * Workspace layout, shared by both attention entry points: the first
  * CPDEC_STEP_COUNTER_BYTES bytes hold cpdec_cp_decode's arrival counters and
- * are never written by cpdec_attn_partial; the chunk partials follow.
+ * are never written by cpdec_attn_partial; then either the chunk partials
+ * (split shards) or the longest-first launch order (32 bytes per (shard,
+ * sequence) pair; see cpdec_attn_order).
  */
 #define CPDEC_STEP_COUNTER_BYTES 65536
 size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
@@ -104,8 +107,9 @@ size_t cpdec_step_workspace_bytes(const cpdec_attn_desc* d);
 
 /*
  * Number of kernel launches cpdec_cp_decode makes for `d`: 1 (the usual case),
- * or 2/3 when a limit of the one-launch form is exceeded (see
- * cpdec_cp_decode).  Errors: the descriptor checks of cpdec_attn_partial.
+ * or 2 to 3 when a limit of the one-launch form is exceeded (see
+ * cpdec_cp_decode), one more for the longest-first order pre-pass (see
+ * cpdec_attn_order).  Errors: the descriptor checks of cpdec_attn_partial.
  */
 cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches);
 
@@ -118,6 +122,25 @@ cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches);
  */
 cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens,
                              int32_t* num_chunks, int32_t* waves);
+
+/*
+ * Whether calls with `d` launch their work longest first (*longest_first =
+ * 1) or in index order (0).  Longest first applies when the library picks the
+ * schedule (chunk_tokens == 0), shards are not split, there are at least 2048
+ * work units (shards x sequences x kv heads x ceil(G/16)), at most 4096
+ * (shard, sequence) pairs and at least 4 GiB of K and V at capacity
+ * (shards x sequences x kv heads x kv_capacity x D x 4 bytes; below that the
+ * pre-pass, about 10 us, outweighs the gain): a one-workgroup pre-pass kernel
+ * sorts the pairs by
+ * lens (longest first, ties in index order) into the workspace, and the
+ * attention kernel takes its units in that order, so that the short units
+ * fill the end of the launch instead of the long ones (ragged batches finish
+ * sooner; every output is the same bit for bit either way, since each unit's
+ * arithmetic does not depend on when it runs).  The pre-pass is one more
+ * launch on the stream.  `longest_first` may be NULL.  Errors: the descriptor
+ * checks of cpdec_attn_partial; the output is untouched on error.
+ */
+cpdec_status cpdec_attn_order(const cpdec_attn_desc* d, int32_t* longest_first);
 
 /*
  * Per-shard decode attention (page section "Introduction").
@@ -146,9 +169,11 @@ cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens,
  *                for the split-KV chunk partials; its contents on entry do not
  *                matter (no clearing is needed, also when one buffer serves
  *                descriptors of different shapes), and the counter region at
- *                its start is left untouched.  When that size is non-zero
- *                the call enqueues two kernels (attention, then the merge of
- *                each shard's chunk partials), otherwise one.
+ *                its start is left untouched.  The call enqueues the
+ *                attention kernel, preceded by the order pre-pass when the
+ *                launch is longest first (cpdec_attn_order) and followed by
+ *                the merge of each shard's chunk partials when shards are
+ *                split.
  *   stream       hipStream_t
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP (see above).
  */
@@ -208,7 +233,8 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  * <= the workgroup's threads, at most 1024 workgroups) or split shards (at
  * most 16 chunks, shards x min(G,16) x D/4 <= the workgroup's threads);
  * otherwise the step runs as attention, chunk-merge and merge launches, where
- * the merge work spreads over many workgroups (cpdec_step_plan tells which).
+ * the merge work spreads over many workgroups, with the order pre-pass of
+ * cpdec_attn_order in front when it applies (cpdec_step_plan tells which).
  * `out` agrees with cpdec_lse_merge of the same partials to rounding.
  *
  *   d, q, k_shards, v_shards, lens, o_part, lse_part, stream

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.cpdec_step_plan.restype = ctypes.c_int
         L.cpdec_attn_plan.argtypes = [ctypes.POINTER(AttnDesc), pi, pi, pi]
         L.cpdec_attn_plan.restype = ctypes.c_int
+        L.cpdec_attn_order.argtypes = [ctypes.POINTER(AttnDesc), pi]
+        L.cpdec_attn_order.restype = ctypes.c_int
         L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
         L.cpdec_attn_partial.restype = ctypes.c_int
@@ -126,12 +128,17 @@ def make_attn_desc(q, k_shards, *, kv_capacity=None, sm_scale=0.0, opart_dtype=N
 
 
 def attn_plan(desc: AttnDesc) -> dict:
-    """The library's launch plan for a descriptor: chunk tokens, chunks, waves."""
-    c, n, wv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    """The library's launch plan for a descriptor: chunk tokens, chunks, waves,
+    and whether the units are launched longest first."""
+    c, n, wv, lf = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     rc = lib().cpdec_attn_plan(ctypes.byref(desc), ctypes.byref(c), ctypes.byref(n), ctypes.byref(wv))
     if rc != 0:
         raise CpdecError(rc, "cpdec_attn_plan")
-    return dict(chunk_tokens=c.value, num_chunks=n.value, waves=wv.value)
+    rc = lib().cpdec_attn_order(ctypes.byref(desc), ctypes.byref(lf))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_attn_order")
+    return dict(chunk_tokens=c.value, num_chunks=n.value, waves=wv.value,
+                longest_first=bool(lf.value))
 
 
 def attn_workspace_bytes(desc: AttnDesc) -> int:

@@ -197,6 +197,7 @@ struct Args {
   int64_t sb, sh, st;
   int32_t B, Hq, Hkv, G, Gb, gblocks, R, chunk, nchunks, units, odt, out_dt, cap;
   float scale_log2;
+  const void* order;  // longest-first launch order (ordered kernels only, else null)
 };
 
 // (readfirstlane afterwards: the compiler takes an asm result for a per-lane
@@ -214,15 +215,35 @@ __device__ __forceinline__ V rfl_v(V x) {
   }
 }
 
+template <bool ORDERED = false>
 __device__ __forceinline__ Args load_args(const AttnParams& p, const void*& kshard,
                                           const void*& vshard) {
   Args a;
+  a.order = nullptr;
   a.q = p.q; a.lens = p.lens; a.o_part = p.o_part; a.lse_part = p.lse_part; a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse; a.out = p.out; a.lse_out = p.lse_out; a.counters = p.counters;
   a.sb = p.sb; a.sh = p.sh; a.st = p.st;
   a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.Gb = p.Gb; a.gblocks = p.gblocks; a.R = p.R;
   a.chunk = p.chunk; a.nchunks = p.nchunks; a.units = p.units; a.odt = p.odt; a.out_dt = p.out_dt;
   a.cap = p.cap; a.scale_log2 = p.scale_log2;
+  if constexpr (ORDERED) {  // the shard pointers come from the order entry instead
+    a.order = p.order;
+    kshard = nullptr;
+    vshard = nullptr;
+    asm volatile(""
+                 : "+s"(a.q), "+s"(a.lens), "+s"(a.o_part), "+s"(a.lse_part), "+s"(a.order),
+                   "+s"(a.sb), "+s"(a.sh), "+s"(a.st), "+s"(a.B), "+s"(a.Hq), "+s"(a.Hkv),
+                   "+s"(a.G), "+s"(a.Gb), "+s"(a.gblocks), "+s"(a.R), "+s"(a.chunk),
+                   "+s"(a.nchunks), "+s"(a.units), "+s"(a.odt), "+s"(a.cap), "+s"(a.scale_log2));
+    a.q = rfl_v(a.q); a.lens = rfl_v(a.lens); a.o_part = rfl_v(a.o_part);
+    a.lse_part = rfl_v(a.lse_part); a.order = rfl_v(a.order);
+    a.sb = rfl_v(a.sb); a.sh = rfl_v(a.sh); a.st = rfl_v(a.st);
+    a.B = rfl_v(a.B); a.Hq = rfl_v(a.Hq); a.Hkv = rfl_v(a.Hkv); a.G = rfl_v(a.G); a.Gb = rfl_v(a.Gb);
+    a.gblocks = rfl_v(a.gblocks); a.R = rfl_v(a.R); a.chunk = rfl_v(a.chunk);
+    a.nchunks = rfl_v(a.nchunks); a.units = rfl_v(a.units); a.odt = rfl_v(a.odt);
+    a.cap = rfl_v(a.cap); a.scale_log2 = rfl_v(a.scale_log2);
+    return a;
+  }
   kshard = p.k[blockIdx.y];
   vshard = p.v[blockIdx.y];
   asm volatile(""
@@ -989,11 +1010,11 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   }
 }
 
-template <typename T, int D, int NW, int MODE>
+template <typename T, int D, int NW, int MODE, bool ORDERED = false>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
   const void* kshard;
   const void* vshard;
-  const Args p = load_args(kp, kshard, vshard);
+  const Args p = load_args<ORDERED>(kp, kshard, vshard);
   __shared__ KernelSmem<T, D, NW, MODE> sh;
   __shared__ int s_last;
   __shared__ int s_nl[MODE >= kStepOneShards ? kMaxShards : 1];  // live chunks per shard
@@ -1003,18 +1024,41 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
   // Workgroups are dealt to the 8 XCDs round-robin by linear block index, so
   // block % 8 must not correlate with the chunk index (the later chunks of
   // ragged shards are mostly empty); here it follows the unit.
-  const int r = blockIdx.y;
   const int upr = p.B * p.Hkv * p.gblocks;  // units per shard
-  const int c = blockIdx.x / upr;
-  const int uis = blockIdx.x - c * upr;
+  int r, c, uis, gb, h, b, len_raw;
+  if constexpr (ORDERED) {
+    // Longest-first order (shards not split): consecutive blocks are the
+    // (kv head, head block) units of one (shard, sequence) pair, and the
+    // pairs come longest first, as the order pre-pass listed them.
+    const int per_pair = p.Hkv * p.gblocks;
+    const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+    const int pair = lin / per_pair;
+    const int hu = lin - pair * per_pair;
+    const rsrc_t ors = make_rsrc(p.order, (uint32_t)(p.R * p.B * sizeof(OrderEntry)));
+    const u32x4 e0 = buf16(ors, (uint32_t)pair * sizeof(OrderEntry));
+    const u32x4 e1 = buf16(ors, (uint32_t)pair * sizeof(OrderEntry) + 16u);
+    kshard = reinterpret_cast<const void*>((uint64_t)rfl(e0[0]) | ((uint64_t)rfl(e0[1]) << 32));
+    vshard = reinterpret_cast<const void*>((uint64_t)rfl(e0[2]) | ((uint64_t)rfl(e0[3]) << 32));
+    r = (int)rfl(e1[0]);
+    b = (int)rfl(e1[1]);
+    len_raw = (int)rfl(e1[2]);
+    c = 0;
+    gb = hu % p.gblocks;
+    h = hu / p.gblocks;
+    uis = b * per_pair + hu;
+  } else {
+    r = blockIdx.y;
+    c = blockIdx.x / upr;
+    uis = blockIdx.x - c * upr;
+    int u = uis;
+    gb = u % p.gblocks; u /= p.gblocks;
+    h = u % p.Hkv;
+    b = u / p.Hkv;
+    // this shard's length (waited for inside, after the first tile is requested)
+    len_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4)), (r * p.B + b) * 4, 0, 0);
+  }
   const int unit = r * upr + uis;
-  int u = uis;
-  const int gb = u % p.gblocks; u /= p.gblocks;
-  const int h = u % p.Hkv;
-  const int b = u / p.Hkv;
-  // this shard's length (waited for inside, after the first tile is requested)
-  const int len_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4)), (r * p.B + b) * 4, 0, 0);
   // One-launch step: every shard's length of this sequence, for whichever
   // workgroup ends up merging (requested early inside, used after the attention).
   int len_t = 0;
@@ -1135,9 +1179,94 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) 
   }
 }
 
+// Longest-first launch order: one workgroup sorts the R*B (shard, sequence)
+// pairs by length, longest first (ties in index order, so the order is
+// deterministic), with a bitonic sort of 64-bit keys in LDS, and writes one
+// OrderEntry per pair.  Lengths are clamped to [0, cap] for the key only.
+// npad = R*B rounded up to a power of two; threads = npad/2 within [64, 1024],
+// so each thread does one compare-exchange per stage (two for npad = 4096).
+constexpr int kOrderMaxThreads = 1024;
+__global__ __launch_bounds__(kOrderMaxThreads) void order_kernel(const AttnParams p, int npad) {
+  __shared__ uint64_t key[kOrderMaxPairs];
+  __shared__ const void* kp[kMaxShards];
+  __shared__ const void* vp[kMaxShards];
+  const int t = threadIdx.x;
+  const int nt = blockDim.x;
+  const int n = p.R * p.B;
+  if (t < p.R) {
+    kp[t] = p.k[t];
+    vp[t] = p.v[t];
+  }
+  for (int i = t; i < npad; i += nt) {
+    uint64_t k = ~0ull;  // padding sorts last
+    if (i < n) {
+      const int L = min(max(p.lens[i], 0), p.cap);
+      k = ((uint64_t)(uint32_t)(0x7fffffff - L) << 32) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  // Stage (size, stride): pair i compares positions lo = 2i - (i mod stride)
+  // and lo + stride, ascending where lo & size == 0.  For stride <= 64 the 64
+  // pairs of a wave (i = 64w + j, in each pass of nt pairs) stay inside the
+  // wave's own 128 positions, so a run of such stages needs no workgroup
+  // barrier, only the wave's own program order; a wider stage, and the first
+  // stage after one, synchronise the workgroup.
+  bool prev_wide = true;
+  for (int size = 2; size <= npad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const bool wide = stride > 64;
+      if (wide || prev_wide) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+      prev_wide = wide;
+      for (int i = t; i < npad / 2; i += nt) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool ascending = (lo & size) == 0;
+        const uint64_t a = key[lo], c = key[hi];
+        if ((a > c) == ascending) {
+          key[lo] = c;
+          key[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += nt) {
+    const int idx = (int)(uint32_t)key[i];
+    const int r = idx / p.B;
+    const int b = idx - r * p.B;
+    const uint64_t kk = reinterpret_cast<uint64_t>(kp[r]), vv = reinterpret_cast<uint64_t>(vp[r]);
+    u32x4* e = reinterpret_cast<u32x4*>(static_cast<char*>(p.order) + (size_t)i * sizeof(OrderEntry));
+    e[0] = u32x4{(uint32_t)kk, (uint32_t)(kk >> 32), (uint32_t)vv, (uint32_t)(vv >> 32)};
+    e[1] = u32x4{(uint32_t)r, (uint32_t)b, (uint32_t)p.lens[idx], 0u};
+  }
+}
+
+hipError_t launch_order(const AttnParams& p, hipStream_t s) {
+  const int n = p.R * p.B;  // <= kOrderMaxPairs (the planner's limit)
+  int npad = 2;
+  while (npad < n) npad <<= 1;
+  const int threads = min(kOrderMaxThreads, max(64, npad / 2));
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(threads), 0, s, p, npad);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int NW>
 hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipStream_t s) {
   const dim3 grid((unsigned)(units / p.R * p.nchunks), (unsigned)p.R), block(NW * 64);
+  if (p.order != nullptr) {  // shards not split, separate launches
+    hipError_t e = launch_order(p, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly, true>), grid, block, 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess || mode != kStepLaunches) return e;
+    return launch_lse_merge(p.o_part, p.lse_part, p.R, (int64_t)p.B * p.Hq, D, p.odt, p.out_dt,
+                            p.out, p.lse_out, s);
+  }
   if (mode == kStepOneShards) {
     hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneShards>), grid, block, 0, s, p);
     return hipGetLastError();

@@ -24,7 +24,9 @@ struct Overrides {
   int waves = 0;   // CPDEC_WAVES: 1, 2, 4 or 8
   int chunk = 0;   // CPDEC_CHUNK: tokens, multiple of 32
   bool step_launches = false;  // CPDEC_STEP_LAUNCHES=1: the whole step as separate launches
+  bool no_order = false;       // CPDEC_ORDER=0: index launch order always
   Overrides() {
+    if (const char* s = getenv("CPDEC_ORDER")) no_order = atoi(s) == 0;
     if (const char* s = getenv("CPDEC_STEP_LAUNCHES")) step_launches = atoi(s) != 0;
     if (const char* s = getenv("CPDEC_WAVES")) {
       int w = atoi(s);
@@ -55,6 +57,8 @@ struct AttnPlan {
   size_t ws_bytes = 0;       // what cpdec_attn_partial needs (0: no workspace)
   size_t step_ws_bytes = 0;  // what cpdec_cp_decode needs (counters + partials)
   size_t off_lse = 0, off_o = 0;
+  size_t off_order = 0;      // longest-first launch order entries (when ordered)
+  bool ordered = false;      // launch (shard, sequence) pairs longest first
   StepMode step = kStepLaunches;  // how cpdec_cp_decode runs
 };
 
@@ -153,6 +157,20 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
           (int64_t)p.Gb * (D / 4) <= threads;
   }
   p.step = !one ? kStepLaunches : (p.nchunks > 1 ? kStepOneChunks : kStepOneShards);
+
+  // Longest-first launch order for large grids of unsplit shards when the
+  // library picks the schedule: the order entries follow the counter region.
+  // (Such grids never take the one-launch step: kOrderMinUnits > kStepUnsplitBlocks.)
+  const double kv_cap_bytes =
+      (double)R * d->batch * d->num_kv_heads * (double)cap * D * 2.0 * 2.0;  // K and V, 16-bit
+  p.ordered = d->chunk_tokens == 0 && !overrides().no_order && p.nchunks == 1 &&
+              p.units >= kOrderMinUnits && R * d->batch <= kOrderMaxPairs &&
+              kv_cap_bytes >= kOrderMinKvBytes;
+  if (p.ordered) {
+    p.off_order = kStepCounterBytes;
+    p.ws_bytes = p.off_order + (size_t)R * d->batch * sizeof(OrderEntry);
+    p.step_ws_bytes = p.ws_bytes;
+  }
   *pl = p;
   return CPDEC_OK;
 }
@@ -179,7 +197,16 @@ cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches) {
   AttnPlan pl;
   const cpdec_status st = plan_attn(d, &pl);
   if (st != CPDEC_OK) return st;
-  if (launches) *launches = pl.step != kStepLaunches ? 1 : (pl.nchunks > 1 ? 3 : 2);
+  if (launches)
+    *launches = pl.step != kStepLaunches ? 1 : (pl.nchunks > 1 ? 3 : 2) + (pl.ordered ? 1 : 0);
+  return CPDEC_OK;
+}
+
+cpdec_status cpdec_attn_order(const cpdec_attn_desc* d, int32_t* longest_first) {
+  AttnPlan pl;
+  const cpdec_status st = plan_attn(d, &pl);
+  if (st != CPDEC_OK) return st;
+  if (longest_first) *longest_first = pl.ordered ? 1 : 0;
   return CPDEC_OK;
 }
 
@@ -261,11 +288,12 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
   p.lens = lens;
   p.o_part = o_part;
   p.lse_part = lse_part;
-  if (pl.ws_bytes > 0) {
+  if (pl.nchunks > 1) {
     char* ws = static_cast<char*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(ws + pl.off_lse);
     p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   }
+  if (pl.ordered) p.order = static_cast<char*>(workspace) + pl.off_order;
   StepMode mode = kPartialsOnly;
   if (so != nullptr) {
     mode = pl.step;

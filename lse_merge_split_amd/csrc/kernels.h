@@ -32,7 +32,30 @@ struct AttnParams {
   float* lse_out;     // [B][Hq] merged lse, may be null
   int32_t out_dt;
   int32_t* counters;  // [B * Hkv * gblocks] arrival counters, zero between calls
+  // longest-first launch order (unsplit shards only): [R * B] OrderEntry, filled
+  // by the order kernel before the attention launch; null: index order
+  void* order;
 };
+
+// One (shard, sequence) pair of the longest-first launch order.
+struct OrderEntry {
+  const void* k;  // the pair's shard K and V base pointers
+  const void* v;
+  int32_t r, b;   // shard, sequence
+  int32_t len;    // lens[r][b] as given
+  int32_t pad;
+};
+static_assert(sizeof(OrderEntry) == 32, "order entry layout");
+
+// Longest-first launch order: when shards are not split and the grid is large,
+// a one-workgroup pre-pass sorts the (shard, sequence) pairs by length,
+// longest first, so that the longest units start first and the short ones
+// fill the end of the launch (longest-processing-time-first scheduling).
+// The pre-pass costs about 10 us (a launch and a sort), so it is used only
+// where the attention is long enough for the schedule to matter.
+constexpr int kOrderMaxPairs = 4096;      // R * B that the one-workgroup sort takes
+constexpr int64_t kOrderMinUnits = 2048;  // smaller grids keep index order
+constexpr double kOrderMinKvBytes = 4294967296.0;  // K+V bytes at capacity, at least
 
 // How a launch treats the cross-shard merge.
 enum StepMode : int {

@@ -84,6 +84,51 @@ def test_step_plan_launches():
     assert cp.lib().cpdec_step_plan(None, None) == INVALID
 
 
+def _order(d):
+    lf = ctypes.c_int32(-1)
+    rc = cp.lib().cpdec_attn_order(ctypes.byref(d), ctypes.byref(lf))
+    return rc, lf.value
+
+
+def test_longest_first_order_plan():
+    """Longest-first launch order: large unsplit grids when the library picks
+    the schedule; the order entries (32 bytes per (shard, sequence) pair)
+    follow the counter region, and the pre-pass is one more launch."""
+    C = cp.STEP_COUNTER_BYTES
+    lib = cp.lib()
+    # 8 shards x 64 sequences x 8 kv heads = 4096 units, 8192 tokens per shard (unsplit)
+    big = dict(batch=64, num_q_heads=32, num_kv_heads=8, num_shards=8, kv_capacity=8192,
+               kv_stride_head=8192 * 128, kv_stride_batch=8 * 8192 * 128)
+    d = _desc(**big)
+    assert _order(d) == (OK, 1)
+    assert cp.attn_plan(d)["num_chunks"] == 1 and cp.attn_plan(d)["longest_first"]
+    assert lib.cpdec_attn_workspace_bytes(ctypes.byref(d)) == C + 8 * 64 * 32
+    assert lib.cpdec_step_workspace_bytes(ctypes.byref(d)) == C + 8 * 64 * 32
+    assert cp.step_launches(d) == 3  # order pre-pass, attention, merge
+    # an explicit chunk length fixes the schedule: index order, no workspace
+    fixed = _desc(chunk_tokens=8192, **big)
+    assert _order(fixed) == (OK, 0)
+    assert lib.cpdec_attn_workspace_bytes(ctypes.byref(fixed)) == 0
+    assert cp.step_launches(fixed) == 2
+    # fewer than 2048 units (here 1024 = 8 x 16 x 8): index order
+    small = dict(big, batch=16, kv_stride_batch=8 * 8192 * 128)
+    assert _order(_desc(**small)) == (OK, 0)
+    # more than 4096 (shard, sequence) pairs: index order
+    many = dict(big, batch=513, num_kv_heads=1, num_q_heads=4, kv_stride_batch=8192 * 128)
+    assert _order(_desc(**many)) == (OK, 0)
+    ok = dict(many, batch=512)
+    assert _order(_desc(**ok)) == (OK, 1)
+    # under 4 GiB of K and V at capacity (8 x 64 x 8 x 512 tokens x 512 B = 1 GiB): index order
+    short = dict(big, kv_capacity=512, kv_stride_head=512 * 128, kv_stride_batch=8 * 512 * 128)
+    assert cp.attn_plan(_desc(**short))["num_chunks"] == 1
+    assert _order(_desc(**short)) == (OK, 0)
+    # split shards never reorder
+    assert _order(_desc()) == (OK, 0)
+    # descriptor errors, output untouched
+    assert _order(_desc(head_dim=96)) == (UNSUPPORTED, -1)
+    assert lib.cpdec_attn_order(None, None) == INVALID
+
+
 # Fake (never dereferenced) device addresses.  Every call below must fail
 # validation, which runs before any HIP call; with a GPU visible a wrong
 # acceptance would launch a kernel on these addresses, so the cases run only

@@ -17,6 +17,7 @@ from synth import gpu as sg  # noqa: E402
 @pytest.mark.parametrize("name,w", [
     ("split shards (chunk merge)", sc.small("c4", B=8, Lcap=700)),
     ("whole shards", sc.small("c3", B=4, Lcap=640, L=600)),
+    ("whole shards, longest first (order pre-pass)", sc.small("c4", B=64, Hq=32, Hkv=8, Lcap=2048)),
     ("merge-only rows", None),
     ("one-launch step, split", sc.small("c4", B=2, Hq=8, Lcap=700)),
     ("one-launch step, whole shards", sc.small("c3", B=8, Lcap=640, L=600)),
