@@ -376,7 +376,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or fused
                                                            or info.get("nchunks", 1) == 1
                                                            else " + attn_combine_kernel")
-                     + (" + order_kernel" if info.get("longest_first") else ""),
+                     + (" + order_kernel" if info.get("longest_first") and not fused else ""),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
