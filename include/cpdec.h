@@ -160,8 +160,10 @@ cpdec_status cpdec_attn_order(const cpdec_attn_desc* d, int32_t* longest_first);
  *   v_shards     same for V (same strides).  Both arrays are read during the
  *                call and not retained.  Every pointer and every stride (in
  *                bytes) must be a multiple of 16.
- *   lens         device, int32 [R][B]; values in [0, kv_capacity] (not
- *                checked on the device; values outside are undefined behaviour)
+ *   lens         device, int32 [R][B]; values in [0, kv_capacity].  The
+ *                kernels clamp to that range (a negative length counts as
+ *                0, one above kv_capacity as kv_capacity), so no value makes
+ *                them read outside the shard; they report nothing about it.
  *   o_part       device, [R][B][Hq][D] contiguous, opart_dtype, 16-byte aligned
  *   lse_part     device, float [R][B][Hq]
  *   workspace    device, at least cpdec_attn_workspace_bytes(d) bytes,

@@ -354,7 +354,8 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
         lens_rs, threadIdx.x < (unsigned)p.R ? (int)((threadIdx.x * p.B + b) * 4) : (int)kOutOfRange, 0,
         0);
   }
-  const int L = __builtin_amdgcn_readfirstlane(len_raw);
+  // lengths outside [0, cap] are taken as the nearest bound (reads stay inside the shard)
+  const int L = min(max(__builtin_amdgcn_readfirstlane(len_raw), 0), p.cap);
   const int t_end = min(L, t_begin + p.chunk);  // <= t_begin for an empty chunk
   const int nlive = (L + p.chunk - 1) / p.chunk;
   const uint32_t span = rows_span(t_end);
@@ -1075,7 +1076,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     // Arrival: this workgroup's device-scope stores are complete before the
     // counter moves; the workgroup that takes the group's counter to its
     // member count (R shards x chunks) merges the group and resets it.
-    if (threadIdx.x < (unsigned)p.R) s_nl[threadIdx.x] = (len_t + p.chunk - 1) / p.chunk;
+    if (threadIdx.x < (unsigned)p.R)
+      s_nl[threadIdx.x] = (min(max(len_t, 0), p.cap) + p.chunk - 1) / p.chunk;
     wait_vm_all();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1121,7 +1123,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams kp) 
   const int h = u % p.Hkv; u /= p.Hkv;
   const int b = u % p.B;
   const int r = u / p.B;
-  const int L = __builtin_amdgcn_readfirstlane(p.lens[r * p.B + b]);  // uniform address
+  const int L = min(max(__builtin_amdgcn_readfirstlane(p.lens[r * p.B + b]), 0), p.cap);
   const int nlive = (L + p.chunk - 1) / p.chunk;
   if (nlive < 2) return;  // written directly by the attention kernel
   const int g0 = gb * kGroupRows;

@@ -64,3 +64,46 @@ def test_outputs_stay_in_bounds(name, w, chunk):
         assert untouched(b, torch.float32 if k != "out" else dt), f"{k} guard overwritten"
     assert bool((wsb[:PAD * 4] == 0x7F).all()) and bool((wsb[-PAD * 4:] == 0x7F).all())
     assert int(torch.count_nonzero(ws[:cp.STEP_COUNTER_BYTES]).item()) == 0
+
+
+@pytest.mark.parametrize("name,w,chunk", [
+    ("split, one launch", sc.small("c4", B=4, Hq=16, Lcap=200), 0),
+    ("split, chunk 32 (separate launches)", sc.small("c4", B=4, Hq=16, Lcap=200), 32),
+    ("unsplit, one launch", sc.small("c4", B=16, Lcap=300), 0),
+])
+def test_lengths_outside_capacity_are_clamped(name, w, chunk):
+    """lens below 0 act as 0 and above the capacity as the capacity, in every
+    form of the call: the results equal those of the clamped lengths bit for
+    bit (the kernels never read outside a shard's tokens)."""
+    print(f"[case] clamped lengths {name}", flush=True)
+    sys.stdout.flush()
+    from tests.helpers import run_path
+    inp = sg.attn_inputs(w)
+    lens = inp["lens_np"].copy()
+    wild = lens.copy()
+    wild[0, 0] = w.Lcap + 1
+    wild[-1, -1] = 2 ** 30
+    wild[0, -1] = -5
+    wild[-1, 0] = -(2 ** 31)
+    lens[0, 0] = w.Lcap
+    lens[-1, -1] = w.Lcap
+    lens[0, -1] = 0
+    lens[-1, 0] = 0
+    clean = dict(inp, lens=torch.from_numpy(lens).cuda())
+    bad = dict(inp, lens=torch.from_numpy(wild).cuda())
+
+    def step(x):
+        R, B, Hq, D = w.R, w.B, w.Hq, w.D
+        res = dict(o_part=torch.empty((R, B, Hq, D), dtype=torch.float32, device="cuda"),
+                   lse_part=torch.empty((R, B, Hq), dtype=torch.float32, device="cuda"),
+                   out=torch.empty((B, Hq, D), dtype=x["q"].dtype, device="cuda"),
+                   lse_out=torch.empty((B, Hq), dtype=torch.float32, device="cuda"))
+        cp.cp_decode(x["q"], x["k_shards"], x["v_shards"], x["lens"], res["o_part"],
+                     res["lse_part"], res["out"], res["lse_out"], chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        return res
+
+    for form, f in (("two calls", lambda x: run_path(x, chunk_tokens=chunk)), ("step", step)):
+        a, b = f(clean), f(bad)
+        for k in a:
+            assert torch.equal(a[k], b[k]), f"{form}: {k} differs with out-of-range lengths"
