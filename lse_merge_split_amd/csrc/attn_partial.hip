@@ -269,7 +269,7 @@ __device__ __forceinline__ Args load_args(const AttnParams& p, const void*& ksha
 // normalised chunk result goes to o_part/lse_part when the unit has one live
 // chunk, else to the workspace.  In the one-launch step modes these stores are
 // device-scope, for the workgroup that merges the group.
-template <typename T, int D, int NW, int MODE>
+template <typename T, int D, int NW, int MODE, bool SPEC2>
 __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, const void* vshard,
                                              Smem<D, NW>& sm, int c, int unit, int r, int b, int h,
                                              int gb, int len_raw, int& len_t) {
@@ -342,11 +342,17 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
     }
   };
 
-  u32x4 kr[2][KS], vr[NB][8];
+  // Tile registers: kt0/vt0 hold the tile being computed; kt1/vt1 are the prefetch
+  // buffer (one tile ahead), or with SPEC2 the second slot of a two-tile ring.
+  u32x4 kt0[2][KS], vt0[NB][8], kt1[2][KS], vt1[NB][8];
   int t0 = t_begin + wave * kTileTokens;
   {
     const uint32_t span0 = rows_span(min(p.cap, t_begin + p.chunk));
-    load_tile(t0, make_rsrc(kb, span0), make_rsrc(vb, span0), kr, vr);
+    const rsrc_t k0 = make_rsrc(kb, span0), v0 = make_rsrc(vb, span0);
+    load_tile(t0, k0, v0, kt0, vt0);
+    // SPEC2 (split shards with several tiles per wave): the second tile too is
+    // requested before the length is known, one memory round trip earlier.
+    if constexpr (SPEC2) load_tile(t0 + NW * kTileTokens, k0, v0, kt1, vt1);
   }
   if constexpr (kDev) {  // every shard's length of this sequence, for the merge (used at the end)
     const rsrc_t lens_rs = make_rsrc(p.lens, (uint32_t)(p.R * p.B * 4));
@@ -361,96 +367,113 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
   const uint32_t span = rows_span(t_end);
   const rsrc_t krs = make_rsrc(kb, span);
   const rsrc_t vrs = make_rsrc(vb, span);
+
+  // One tile at t0: scores, online softmax, p.V into the accumulators.
+  auto tile_step = [&](u32x4 (&kr)[2][KS], u32x4 (&vr)[NB][8]) {
+      // ---- scores S^T (16 tokens x 16 heads per block), base-2 scaled, masked ----
+      float x[2][4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = mfma16x16x32<T>(kr[blk][s], qop[s], sacc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * blk + 4 * q4 + i;
+          x[blk][i] = (t < t_end) ? sacc[i] * p.scale_log2 : neg_inf();
+        }
+      }
+
+      // ---- online softmax for head g = l16 ----
+      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      {  // over the 4 lane rows (q4) holding head g's tokens
+        const f32x2 a = rows16(mt);
+        mt = fmaxf(a[0], a[1]);
+        const f32x2 c = rows32(mt);
+        mt = fmaxf(c[0], c[1]);
+      }
+      const float m_new = fmaxf(m, mt);  // -inf only while every token so far was masked
+      const float m_ref = m_new == neg_inf() ? 0.f : m_new;  // keeps -inf - -inf out
+      const float alpha = exp2f(m - m_ref);
+      // rescale the accumulators only when some head's running max grew
+      // (rare after the first tiles); the branch is wave-uniform and holds no loads
+      const bool grew = __any(m_new > m);
+      m = m_new;
+      float pr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_ref);
+      float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      lsum = lsum * alpha + ps;
+
+      // A tile crossing the end: V rows past it (padding read by the first,
+      // speculative load) become zeros, since 0 * NaN would poison the sums.
+      if (t0 + kTileTokens > t_end) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool dead = t0 + tile_token(q4, j) >= t_end;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (dead) vr[nb][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+
+      // P operand (B of O^T = V^T P^T), split into hi + lo 16-bit parts.
+      u32x4 phi, plo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t hw = pack2<T>(pr[2 * k], pr[2 * k + 1]);
+        phi[k] = hw;
+        plo[k] = pack2<T>(pr[2 * k] - lo_of<T>(hw), pr[2 * k + 1] - hi_of<T>(hw));
+      }
+
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          // V^T operand row (d = 8*(16 nb + l16) + n), tokens tile_token(q4, 0..7).
+          const int w = n >> 1;
+          const uint32_t sel = (n & 1) ? kSelHiHalves : kSelLoHalves;
+          u32x4 va;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) va[k] = perm_b32(vr[nb][2 * k + 1][w], vr[nb][2 * k][w], sel);
+          f32x4 a = grew ? acc[nb][n] * alpha : acc[nb][n];
+          a = mfma16x16x32<T>(va, phi, a);
+          acc[nb][n] = mfma16x16x32<T>(va, plo, a);
+        }
+      }
+  };
+
   // The first tile is always processed (fully masked when the wave's part of
   // the chunk is empty): no branch may separate its loads from their use, or
   // the compiler moves the loads behind the length check.
-  do {
-    // prefetch the wave's next tile while this one is computed
-    u32x4 krn[2][KS], vrn[NB][8];
-    load_tile(t0 + NW * kTileTokens, krs, vrs, krn, vrn);
-
-    // ---- scores S^T (16 tokens x 16 heads per block), base-2 scaled, masked ----
-    float x[2][4];
+  if constexpr (SPEC2) {
+    // Two slots with fixed roles (no register copies of tiles in flight): a
+    // slot is refilled with the tile two steps ahead as soon as it is consumed.
+    do {
+      tile_step(kt0, vt0);
+      load_tile(t0 + 2 * NW * kTileTokens, krs, vrs, kt0, vt0);
+      t0 += NW * kTileTokens;
+      if (t0 >= t_end) break;
+      tile_step(kt1, vt1);
+      load_tile(t0 + 2 * NW * kTileTokens, krs, vrs, kt1, vt1);
+      t0 += NW * kTileTokens;
+    } while (t0 < t_end);
+  } else {
+    do {
+      load_tile(t0 + NW * kTileTokens, krs, vrs, kt1, vt1);  // prefetch the wave's next tile
+      tile_step(kt0, vt0);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc = mfma16x16x32<T>(kr[blk][s], qop[s], sacc);
+        for (int s = 0; s < KS; ++s) kt0[blk][s] = kt1[blk][s];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * blk + 4 * q4 + i;
-        x[blk][i] = (t < t_end) ? sacc[i] * p.scale_log2 : neg_inf();
-      }
-    }
-
-    // ---- online softmax for head g = l16 ----
-    float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    {  // over the 4 lane rows (q4) holding head g's tokens
-      const f32x2 a = rows16(mt);
-      mt = fmaxf(a[0], a[1]);
-      const f32x2 c = rows32(mt);
-      mt = fmaxf(c[0], c[1]);
-    }
-    const float m_new = fmaxf(m, mt);  // -inf only while every token so far was masked
-    const float m_ref = m_new == neg_inf() ? 0.f : m_new;  // keeps -inf - -inf out
-    const float alpha = exp2f(m - m_ref);
-    // rescale the accumulators only when some head's running max grew
-    // (rare after the first tiles); the branch is wave-uniform and holds no loads
-    const bool grew = __any(m_new > m);
-    m = m_new;
-    float pr[8];
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_ref);
-    float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-    lsum = lsum * alpha + ps;
-
-    // A tile crossing the end: V rows past it (padding read by the first,
-    // speculative load) become zeros, since 0 * NaN would poison the sums.
-    if (t0 + kTileTokens > t_end) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool dead = t0 + tile_token(q4, j) >= t_end;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          if (dead) vr[nb][j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-
-    // P operand (B of O^T = V^T P^T), split into hi + lo 16-bit parts.
-    u32x4 phi, plo;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t hw = pack2<T>(pr[2 * k], pr[2 * k + 1]);
-      phi[k] = hw;
-      plo[k] = pack2<T>(pr[2 * k] - lo_of<T>(hw), pr[2 * k + 1] - hi_of<T>(hw));
-    }
-
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        // V^T operand row (d = 8*(16 nb + l16) + n), tokens tile_token(q4, 0..7).
-        const int w = n >> 1;
-        const uint32_t sel = (n & 1) ? kSelHiHalves : kSelLoHalves;
-        u32x4 va;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) va[k] = perm_b32(vr[nb][2 * k + 1][w], vr[nb][2 * k][w], sel);
-        f32x4 a = grew ? acc[nb][n] * alpha : acc[nb][n];
-        a = mfma16x16x32<T>(va, phi, a);
-        acc[nb][n] = mfma16x16x32<T>(va, plo, a);
-      }
-    }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kr[blk][s] = krn[blk][s];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vr[nb][j] = vrn[nb][j];
-    t0 += NW * kTileTokens;
-  } while (t0 < t_end);
+        for (int j = 0; j < 8; ++j) vt0[nb][j] = vt1[nb][j];
+      t0 += NW * kTileTokens;
+    } while (t0 < t_end);
+  }
   if (t_begin >= L) return false;  // empty chunk: nothing is written
 
   {
@@ -1011,7 +1034,7 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   }
 }
 
-template <typename T, int D, int NW, int MODE, bool ORDERED = false>
+template <typename T, int D, int NW, int MODE, bool ORDERED = false, bool SPEC2 = false>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
   const void* kshard;
   const void* vshard;
@@ -1063,7 +1086,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
   // One-launch step: every shard's length of this sequence, for whichever
   // workgroup ends up merging (requested early inside, used after the attention).
   int len_t = 0;
-  if (!attend_chunk<T, D, NW, MODE>(p, kshard, vshard, sh.a, c, unit, r, b, h, gb, len_raw, len_t) &&
+  if (!attend_chunk<T, D, NW, MODE, SPEC2>(p, kshard, vshard, sh.a, c, unit, r, b, h, gb, len_raw,
+                                           len_t) &&
       c == 0) {  // empty shard: o_r = 0, lse_r = -inf (the merge never reads them)
     const int g0 = gb * kGroupRows;
     const int ng = min(kGroupRows, p.G - g0);
@@ -1274,7 +1298,12 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
     return hipGetLastError();
   }
   if (mode == kStepOneChunks) {
-    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks>), grid, block, 0, s, p);
+    // two or more tiles per wave: request the second tile with the first
+    if (p.chunk >= 2 * NW * kTileTokens)
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks, false, true>), grid, block, 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks>), grid, block, 0, s, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);
