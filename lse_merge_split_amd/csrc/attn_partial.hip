@@ -595,10 +595,13 @@ __device__ __forceinline__ void shard_weights(int R, int ng, MergeSmem<NW, MODE>
   for (int pi = threadIdx.x; pi < R * ng; pi += NW * 64) {
     const int g = pi % ng;
     float M = neg_inf();
-    for (int r0 = 0; r0 < R; r0 += 8)  // 8 LDS reads in flight
+    for (int r0 = 0; r0 < R; r0 += 8) {  // 8 LDS reads in flight (no read inside a branch)
+      float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (r0 + j < R) M = fmaxf(M, ms.lse[(r0 + j) * ng + g]);
+      for (int j = 0; j < 8; ++j) v[j] = ms.lse[min(r0 + j, R - 1) * ng + g];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, r0 + j < R ? v[j] : neg_inf());
+    }
     const float l = ms.lse[pi];
     ms.ew[pi] = l == neg_inf() ? 0.0 : exp((double)l - (double)M);
     if (pi < ng) ms.M[pi] = M;
@@ -614,26 +617,34 @@ __device__ __forceinline__ void merge_vector(const Args& p, int64_t row0, int e,
   constexpr int Q = D / 4;
   const int g = e / Q, qd = e % Q;
   const int64_t row = row0 + g;
+  // Reads are issued 8 at a time outside branches; an empty shard has weight
+  // 0 and a zero vector (never read from memory), so it adds exactly nothing.
   double S = 0.0;
-  for (int r0 = 0; r0 < R; r0 += 8)
+  for (int r0 = 0; r0 < R; r0 += 8) {
+    double w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (r0 + j < R) S += ms.ew[(r0 + j) * ng + g];
+    for (int j = 0; j < 8; ++j) w[j] = ms.ew[min(r0 + j, R - 1) * ng + g];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) S += r0 + j < R ? w[j] : 0.0;
+  }
   if (S == 0.0) {
     store4(p.out, row * D + 4 * qd, f32x4{0.f, 0.f, 0.f, 0.f}, p.out_dt);
     if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = neg_inf();
     return;
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < R; r0 += 8)
+  for (int r0 = 0; r0 < R; r0 += 8) {
+    float w[8];
+    f32x4 yv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int r = r0 + j;
-      if (r < R) {
-        const double ew = ms.ew[r * ng + g];
-        if (ew != 0.0) acc += (float)ew * y(r);
-      }
+      const int r = min(r0 + j, R - 1);
+      w[j] = r0 + j < R ? (float)ms.ew[r * ng + g] : 0.f;
+      yv[j] = y(r);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += w[j] * yv[j];
+  }
   store4(p.out, row * D + 4 * qd, acc * (float)(1.0 / S), p.out_dt);
   if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (float)((double)ms.M[g] + log(S));
 }
@@ -691,19 +702,20 @@ __device__ void merge_shards(const Args& p, int b, int h, int gb, const int* s_n
       const int64_t row = row0 + g;
       double S = 0.0;
 #pragma unroll
-      for (int j = 0; j < RB; ++j)
-        if (j < R) S += ms.ew[j * ng + g];
+      for (int j = 0; j < RB; ++j) {
+        const double w = ms.ew[min(j, R - 1) * ng + g];
+        S += j < R ? w : 0.0;
+      }
       if (S == 0.0) {
         store4(p.out, row * D + 4 * qd, f32x4{0.f, 0.f, 0.f, 0.f}, p.out_dt);
         if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = neg_inf();
         continue;
       }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // shards j >= R: weight 0, vector 0 (out of range)
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
-        if (j >= R) break;
-        const double ew = ms.ew[j * ng + g];
-        if (ew != 0.0) acc += (float)ew * pre[j];
+        const float w = j < R ? (float)ms.ew[min(j, R - 1) * ng + g] : 0.f;
+        acc += w * pre[j];
       }
       store4(p.out, row * D + 4 * qd, acc * (float)(1.0 / S), p.out_dt);
       if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (float)((double)ms.M[g] + log(S));
@@ -865,11 +877,15 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
         const float* wr = ms.w + (r * ng + e / Q) * nch;
         const uint32_t base = vec_base(r, e);
         int c0 = part_id;
-        if (i0 == 0) {  // the prefetched first batch
+        if (i0 == 0) {  // the prefetched first batch (weights read first, no branch per chunk)
+          float wv[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) wv[j] = wr[min(c0 + j * P, nch - 1)];
 #pragma unroll
           for (int j = 0; j < KB; ++j) {
-            const int cc = c0 + j * P;
-            if (cc < nl) y += wr[cc] * pre[j];
+            const f32x4 yj = y + wv[j] * pre[j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = c0 + j * P < nl ? yj[k] : y[k];
           }
           c0 += KB * P;
         }
@@ -880,10 +896,14 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
             const int cc = c0 + j * P;
             v[j] = __builtin_bit_cast(f32x4, ld16_dev(wo_rs, cc < nl ? base + cc * cstride : kOutOfRange));
           }
+          float wv[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) wv[j] = wr[min(c0 + j * P, nch - 1)];
 #pragma unroll
           for (int j = 0; j < KB; ++j) {
-            const int cc = c0 + j * P;
-            if (cc < nl) y += wr[cc] * v[j];
+            const f32x4 yj = y + wv[j] * v[j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = c0 + j * P < nl ? yj[k] : y[k];
           }
         }
       } else if (nl == 1 && part_id == 0) {
@@ -995,18 +1015,22 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   __syncthreads();
 
   // ---- (3) shard vectors ----
+  // All weights are read first and the sum is branch-free: a read inside a
+  // per-chunk branch would wait for the LDS on its own, 16 times in a row.
   f32x4 y = {0.f, 0.f, 0.f, 0.f};
   if (ri < R) {
-    if (nli >= 2) {
-      const float* wr = ms.w + ri * nch;
+    const float* wr = ms.w + ri * nch;
+    float wv[KB];
 #pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        const int cc = part + j * P;
-        if (cc < nli) y += wr[cc] * v[j];
-      }
-    } else if (nli == 1) {
-      y = v_one;
+    for (int j = 0; j < KB; ++j) wv[j] = wr[min(part + j * P, nch - 1)];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const bool live = nli >= 2 && part + j * P < nli;  // else wv[j] may be stale
+      const f32x4 yj = y + wv[j] * v[j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = live ? yj[k] : y[k];
     }
+    if (nli == 1) y = v_one;
   }
   if (P > 1) {
     ms.part[t] = y;
@@ -1024,12 +1048,12 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   __syncthreads();
 
   // ---- (4) cross-shard merge, shard order ----
+  // An empty shard has weight 0 and vector 0, so it adds exactly nothing; the
+  // sum needs no branch and its reads can be issued together.
   if (t < Q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < R; ++r) {
-      const float w = ms.lse[r];
-      if (w != 0.f) acc += w * ms.y[r * Q + t];
-    }
+#pragma unroll 4
+    for (int r = 0; r < R; ++r) acc += ms.lse[r] * ms.y[r * Q + t];
     store4(p.out, (int64_t)row0 * D + 4 * t, acc * ms.M[0], p.out_dt);
   }
 }
