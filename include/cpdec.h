@@ -233,8 +233,12 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  * round of loads: groups (sequences x kv heads x ceil(G/16)) <= 1024, o_part
  * below 2 GiB, and either unsplit shards (at most 8 shards, min(G,16) x D/4
  * <= the workgroup's threads, at most 1024 workgroups) or split shards (at
- * most 16 chunks, shards x min(G,16) x D/4 <= the workgroup's threads);
- * otherwise the step runs as attention, chunk-merge and merge launches, where
+ * most 16 chunks, shards x min(G,16) x D/4 <= the workgroup's threads).
+ * Split groups beyond that still take one launch in two levels -- the last
+ * chunk workgroup of each (shard, sequence, kv head) combines its chunks,
+ * the last of the group's shards merges them -- when min(G,16) x D/4 <= the
+ * workgroup's threads, at most 64 chunks and units + groups <= 1024.
+ * Otherwise the step runs as attention, chunk-merge and merge launches, where
  * the merge work spreads over many workgroups, with the order pre-pass of
  * cpdec_attn_order in front when it applies (cpdec_step_plan tells which).
  * `out` agrees with cpdec_lse_merge of the same partials to rounding.

@@ -117,7 +117,7 @@ struct Smem {
 // attention's LDS: it is used only after the workgroup's own chunk is done).
 template <int NW, int MODE>
 struct MergeSmem {
-  static constexpr bool kChunks = MODE == kStepOneChunks;
+  static constexpr bool kChunks = MODE == kStepOneChunks || MODE == kStepTwoLevel;
   float w[kChunks ? kStepSlots : 1];    // chunk weights, [(r * ng + g) * nchunks + c]
   f32x4 y[kChunks ? kStepVecs : 1];     // shard partials as stored, [r * E + e]
   f32x4 part[kChunks ? NW * 64 : 1];    // partition sums
@@ -655,9 +655,9 @@ __device__ __forceinline__ void merge_vector(const Args& p, int64_t row0, int e,
 // (no tokens) are never read.  s_nl[r] = live chunks (0 or 1) of shard r.
 // The shard vectors of this thread's first output vector are loaded together
 // with the lse values (one memory round trip).
-template <int D, int NW>
+template <int D, int NW, int MODE>
 __device__ void merge_shards(const Args& p, int b, int h, int gb, const int* s_nl,
-                             MergeSmem<NW, kStepOneShards>& ms) {
+                             MergeSmem<NW, MODE>& ms) {
   constexpr int NT = NW * 64;
   constexpr int Q = D / 4;  // float4 outputs per head
   constexpr int RB = 8;     // shard vectors loaded per batch
@@ -1058,6 +1058,118 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   }
 }
 
+// One arrival at a counter of `members` arrivals (relaxed, agent scope; the
+// caller's device-scope stores have completed).  Returns whether this was the
+// last arrival, and then resets the counter to zero for the next call.
+__device__ __forceinline__ int arrive(int32_t* counter, int members) {
+  const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int last = old == members - 1;
+  if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// The 4 values x as stored in dtype `odt`, written with a device-scope store at
+// byte offset `off`.
+__device__ __forceinline__ void store4_dev(rsrc_t r, uint32_t off, f32x4 x, int odt) {
+  if (odt == kF32) {
+    st16_dev(r, off, __builtin_bit_cast(u32x4, x));
+  } else if (odt == kBF16) {
+    st8_dev(r, off, u32x2{pack2<bf16_t>(x[0], x[1]), pack2<bf16_t>(x[2], x[3])});
+  } else {
+    st8_dev(r, off, u32x2{pack2<f16_t>(x[0], x[1]), pack2<f16_t>(x[2], x[3])});
+  }
+}
+
+// First level of the two-level one-launch step: the chunk combine of one unit
+// (shard r, sequence b, kv head h, head block gb) with nl >= 2 live chunks,
+// done by the unit's last-arriving chunk workgroup.  Same arithmetic as the
+// chunk-combine launch (per head: chunk max, weights e^(lse_c - M) / sum,
+// shard lse M + ln sum; the weighted sum of the normalised chunk partials),
+// written to o_part/lse_part with device-scope stores for the second level.
+// Chunk statistics: lanes (head g, chunk c) with nlp = nl rounded up to a
+// power of two lanes per head (xor-shuffle reductions within a wave); the
+// weighted sums: threads (partition, head, float4), chunks split over P
+// partitions added in a fixed order.
+template <int D, int NW, int MODE>
+__device__ void combine_unit(const Args& p, int unit, int r, int b, int h, int gb, int nl,
+                             MergeSmem<NW, MODE>& ms) {
+  if (nl < 2) return;  // one live chunk went straight to o_part; none: the shard is empty
+  constexpr int NT = NW * 64;
+  constexpr int Q = D / 4;
+  constexpr int KB = 16;  // chunk vectors in flight per thread
+  const int t = threadIdx.x;
+  const int g0 = gb * kGroupRows;
+  const int ng = min(kGroupRows, p.G - g0);
+  const int nch = p.nchunks;
+  const uint32_t es = esize(p.odt);
+  const int64_t nslots = (int64_t)p.units * nch * p.Gb;
+  const rsrc_t wo_rs = make_rsrc(p.ws_o, (uint32_t)(nslots * D * 4));
+  const rsrc_t wl_rs = make_rsrc(p.ws_lse, (uint32_t)(nslots * 4));
+  const rsrc_t o_rs = make_rsrc(p.o_part, (uint32_t)((int64_t)p.R * p.B * p.Hq * D * es));
+  const rsrc_t l_rs = make_rsrc(p.lse_part, (uint32_t)((int64_t)p.R * p.B * p.Hq * 4));
+  const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;  // o_part row of head g0
+  const int64_t slot0 = (int64_t)unit * nch;                          // chunk 0 of this unit
+
+  // (1) chunk weights and shard lse per head
+  int lg = 0;
+  while ((1 << lg) < nl) ++lg;  // nl <= 64: one wave holds a head's chunks
+  const int nlp = 1 << lg;
+  const int hpp = NT / nlp;  // heads per pass
+  for (int gp = 0; gp < ng; gp += hpp) {
+    const int g = gp + t / nlp, c = t % nlp;
+    const bool on = g < ng && c < nl;
+    float lv = ld4f_dev(wl_rs, on ? (uint32_t)(((slot0 + c) * p.Gb + g) * 4) : kOutOfRange);
+    lv = on ? lv : neg_inf();
+    const float M = lane_reduce(lv, lg, OpMax{});  // finite: a live chunk has tokens
+    const float e = on ? expf(lv - M) : 0.f;
+    const float S = lane_reduce(e, lg, OpSum{});
+    if (on) ms.w[g * nch + c] = e * (1.0f / S);
+    if (c == 0 && g < ng) st4_dev(l_rs, (uint32_t)((orow0 + g) * 4), M + logf(S));
+  }
+  __syncthreads();
+
+  // (2) weighted sums of the chunk partials
+  const int E = ng * Q;
+  int P = 1;
+  while (P < 8 && E * P * 2 <= NT) P *= 2;
+  const int per = NT / P;
+  const int part = t / per;
+  for (int e0 = 0; e0 < E; e0 += per) {
+    const int e = e0 + t % per;
+    const int g = min(e / Q, ng - 1), q = e % Q;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    if (e < E) {
+      const float* wr = ms.w + g * nch;
+      const uint32_t base = (uint32_t)((slot0 * p.Gb + g) * D * 4) + 16u * q;
+      const uint32_t cstride = (uint32_t)(p.Gb * D * 4);
+      for (int c0 = part; c0 < nl; c0 += KB * P) {
+        f32x4 v[KB];
+        float wv[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          const int cc = c0 + j * P;
+          v[j] = __builtin_bit_cast(f32x4, ld16_dev(wo_rs, cc < nl ? base + cc * cstride : kOutOfRange));
+          wv[j] = wr[min(cc, nch - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          const f32x4 yj = y + wv[j] * v[j];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) y[k] = c0 + j * P < nl ? yj[k] : y[k];
+        }
+      }
+    }
+    if (P > 1) {
+      ms.part[t] = y;
+      __syncthreads();
+      if (part == 0)
+        for (int k = 1; k < P; ++k) y += ms.part[t + k * per];
+      __syncthreads();
+    }
+    if (part == 0 && e < E) store4_dev(o_rs, (uint32_t)(((orow0 + g) * D + 4 * q) * es), y, p.odt);
+  }
+}
+
 template <typename T, int D, int NW, int MODE, bool ORDERED = false, bool SPEC2 = false>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
   const void* kshard;
@@ -1128,26 +1240,37 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
       s_nl[threadIdx.x] = (min(max(len_t, 0), p.cap) + p.chunk - 1) / p.chunk;
     wait_vm_all();
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const int grp = ((b * p.Hkv + h) * p.gblocks + gb) * kStepCounterStride;
-      const int members = p.R * p.nchunks;
-      const int old =
-          __hip_atomic_fetch_add(p.counters + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == members - 1;
-      if (last) __hip_atomic_store(p.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    if constexpr (MODE == kStepOneShards) {
+    const int grp = (b * p.Hkv + h) * p.gblocks + gb;
+    if constexpr (MODE == kStepTwoLevel) {
+      // Level 1: the unit's chunk workgroups (counter line `unit`); the last
+      // one combines the unit's chunks into o_part/lse_part.
+      if (threadIdx.x == 0) s_last = arrive(p.counters + unit * kStepCounterStride, p.nchunks);
+      __syncthreads();
+      if (!s_last) return;
+      combine_unit<D, NW>(p, unit, r, b, h, gb, s_nl[r], sh.m);
+      wait_vm_all();
+      __syncthreads();
+      // Level 2: the group's units, one per shard (counter lines after the
+      // units'); the last one merges the shards.
+      if (threadIdx.x == 0)
+        s_last = arrive(p.counters + (p.units + grp) * kStepCounterStride, p.R);
+      __syncthreads();
+      if (!s_last) return;
       merge_shards<D, NW>(p, b, h, gb, s_nl, sh.m);
     } else {
-      int lg_nchp = 0;
-      while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
-      if (p.G == 1 && (p.R << lg_nchp) <= 64)
-        merge_chunks_g1<D, NW>(p, b, h, s_nl, sh.m, lg_nchp);
-      else
-        merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
+      if (threadIdx.x == 0) s_last = arrive(p.counters + grp * kStepCounterStride, p.R * p.nchunks);
+      __syncthreads();
+      if (!s_last) return;
+      if constexpr (MODE == kStepOneShards) {
+        merge_shards<D, NW>(p, b, h, gb, s_nl, sh.m);
+      } else {
+        int lg_nchp = 0;
+        while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
+        if (p.G == 1 && (p.R << lg_nchp) <= 64)
+          merge_chunks_g1<D, NW>(p, b, h, s_nl, sh.m, lg_nchp);
+        else
+          merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
+      }
     }
   }
 }
@@ -1328,6 +1451,14 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
                          s, p);
     else
       hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  if (mode == kStepTwoLevel) {
+    if (p.chunk >= 2 * NW * kTileTokens)
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepTwoLevel, false, true>), grid, block, 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepTwoLevel>), grid, block, 0, s, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);

@@ -156,7 +156,17 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
     one = one && p.units <= kStepUnsplitBlocks && R <= kStepMaxShardsUnsplit &&
           (int64_t)p.Gb * (D / 4) <= threads;
   }
-  p.step = !one ? kStepLaunches : (p.nchunks > 1 ? kStepOneChunks : kStepOneShards);
+  // Split groups too big for one merging workgroup: two levels in the same
+  // launch (chunk combine per unit, then the shard merge per group), with one
+  // counter line per unit and one per group, when each level's output vectors
+  // (min(G,16) x D/4) fit the workgroup's threads -- with a second pass per
+  // level the separate launches measured faster (GQA 8 at D=128: 57 vs 54 us).
+  const bool two = !one && p.nchunks > 1 && !overrides().step_launches &&
+                   p.units + groups <= kStepCounters && p.nchunks <= kStepTwoLevelMaxChunks &&
+                   (int64_t)p.Gb * (D / 4) <= threads && opart_bytes < (1ull << 31) &&
+                   slots * (size_t)D * sizeof(float) < (1ull << 31);
+  p.step = one ? (p.nchunks > 1 ? kStepOneChunks : kStepOneShards)
+               : (two ? kStepTwoLevel : kStepLaunches);
 
   // Longest-first launch order for large grids of unsplit shards when the
   // library picks the schedule: the order entries follow the counter region.

@@ -198,6 +198,9 @@ constexpr int kPolicyDevice = 16;
 __device__ __forceinline__ void st16_dev(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyDevice);
 }
+__device__ __forceinline__ void st8_dev(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kPolicyDevice);
+}
 __device__ __forceinline__ void st4_dev(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kPolicyDevice);
 }

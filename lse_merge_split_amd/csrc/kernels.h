@@ -65,6 +65,10 @@ enum StepMode : int {
                        // shard workgroup of a (sequence, kv head) merges
   kStepOneChunks = 3,  // whole step in one launch, shards split into chunks:
                        // the last chunk workgroup combines chunks and merges
+  kStepTwoLevel = 4,   // whole step in one launch, shards split, group too big
+                       // for one merging workgroup: the last chunk workgroup of
+                       // a unit combines its chunks, the last unit of a group
+                       // merges the shards
 };
 
 // Limits of the one-launch step.  The workgroup that merges a group fetches
@@ -82,6 +86,8 @@ constexpr int kStepMaxShardsUnsplit = 8;    // shards, unsplit
 constexpr int kStepSlots = 2048;            // shards * chunks * heads of one group
 constexpr int kStepVecs = 512;              // shards * heads * D/4 of one group (<= threads)
 constexpr int64_t kStepUnsplitBlocks = 1024; // unsplit shards: one launch up to this grid
+constexpr int kStepTwoLevelMaxChunks = 64;   // chunks per shard in the two-level form (lanes
+                                             // of one wave per head in the chunk statistics)
 
 // Launch the partial-attention kernel over (units / R) x nchunks x R workgroups and
 // whatever else `mode` needs (chunk combine and merge kernels for
