@@ -934,16 +934,18 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
     merge_vector<D>(p, row0, e, R, ng, ms, [&](int r) { return ms.y[r * E + e]; });
 }
 
-// Merge of a split group with one query head (G == 1) whose (shard, chunk)
-// pairs fit one wave: lanes of wave 0 hold one chunk lse each (shard r in
-// lanes [r * nchp, (r + 1) * nchp), nchp = chunks rounded up to a power of
-// two), so every statistic is an xor-shuffle reduction; threads
-// (partition, shard, float4) sum their chunk vectors from registers.  Same
-// formulas as merge_chunks (chunk max, weights, shard lse; FP64 cross-shard
-// weights and lse), with the shuffle trees' summation order.
-template <int D, int NW>
-__device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
-                                MergeSmem<NW, kStepOneChunks>& ms, int lg_nchp) {
+// Chunk combine and cross-shard merge of ONE query head (head g of head block
+// gb of kv head h, sequence b) whose (shard, chunk) pairs fit one wave: lanes
+// of wave 0 hold one chunk lse each (shard r in lanes [r * nchp, (r + 1) *
+// nchp), nchp = chunks rounded up to a power of two), so every statistic is
+// an xor-shuffle reduction; threads (partition, shard, float4) sum their
+// chunk vectors from registers.  Same formulas as merge_chunks (chunk max,
+// weights, shard lse; FP64 cross-shard weights and lse), with the shuffle
+// trees' summation order.  Needs R * Q <= threads and every live chunk among
+// the 16 * P a thread group loads (both hold where it is called).
+template <int D, int NW, int MODE>
+__device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, const int* s_nl,
+                                 MergeSmem<NW, MODE>& ms, int lg_nchp) {
   constexpr int NT = NW * 64;
   constexpr int Q = D / 4;
   constexpr int LGQ = __builtin_ctz(Q);
@@ -954,15 +956,16 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   const int nch = p.nchunks;
   const int nchp = 1 << lg_nchp;
   const uint32_t es = esize(p.odt);
-  const int64_t nslots = (int64_t)p.units * nch;  // Gb == 1
+  const int Gb = p.Gb;
+  const int64_t nslots = (int64_t)p.units * nch * Gb;
   const rsrc_t o_rs = make_rsrc(p.o_part, (uint32_t)((int64_t)R * p.B * p.Hq * D * es));
   const rsrc_t l_rs = make_rsrc(p.lse_part, (uint32_t)((int64_t)R * p.B * p.Hq * 4));
   const rsrc_t wo_rs = make_rsrc(p.ws_o, (uint32_t)(nslots * D * 4));
   const rsrc_t wl_rs = make_rsrc(p.ws_lse, (uint32_t)(nslots * 4));
-  const int row0 = b * p.Hq + h;             // G == 1: query head h
-  const int rstride = p.B * p.Hq;            // o_part rows from shard to shard
-  const int sstride = p.B * p.Hkv * nch;     // workspace slots from shard to shard
-  const int slot00 = (b * p.Hkv + h) * nch;  // shard 0, chunk 0
+  const int row0 = b * p.Hq + h * p.G + gb * kGroupRows + g;    // the query head's row
+  const int rstride = p.B * p.Hq;                                // o_part rows, shard to shard
+  const int sstride = p.B * p.Hkv * p.gblocks * nch;             // slots, shard to shard
+  const int slot00 = ((b * p.Hkv + h) * p.gblocks + gb) * nch;   // shard 0, chunk 0
 
   // items (shard, float4): per = power of two >= R * Q threads, P partitions
   int lg_per = LGQ;
@@ -978,16 +981,18 @@ __device__ void merge_chunks_g1(const Args& p, int b, int h, const int* s_nl,
   const int nll = rl < R ? s_nl[rl] : 0;
   const bool chunk_l = t < 64 && nll >= 2 && cl < nll;  // a live chunk of a split shard
   const bool shard_l = t < 64 && nll == 1 && cl == 0;   // a shard with one live chunk
-  const float lc = ld4f_dev(wl_rs, chunk_l ? (uint32_t)((slot00 + rl * sstride + cl) * 4) : kOutOfRange);
+  const float lc =
+      ld4f_dev(wl_rs, chunk_l ? (uint32_t)(((slot00 + rl * sstride + cl) * Gb + g) * 4) : kOutOfRange);
   const float ls1 = ld4f_dev(l_rs, shard_l ? (uint32_t)((rl * rstride + row0) * 4) : kOutOfRange);
   f32x4 v[KB];
   {
-    const uint32_t base = (uint32_t)((slot00 + ri * sstride) * D * 4) + 16u * qi;
+    const uint32_t base = (uint32_t)(((slot00 + ri * sstride) * Gb + g) * D * 4) + 16u * qi;
+    const uint32_t cstride = (uint32_t)(Gb * D * 4);  // chunk to chunk
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int cc = part + j * P;
       v[j] = __builtin_bit_cast(
-          f32x4, ld16_dev(wo_rs, (nli >= 2 && cc < nli) ? base + (uint32_t)cc * (D * 4) : kOutOfRange));
+          f32x4, ld16_dev(wo_rs, (nli >= 2 && cc < nli) ? base + (uint32_t)cc * cstride : kOutOfRange));
     }
   }
   const f32x4 v_one = load4_dev(
@@ -1267,12 +1272,37 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         int lg_nchp = 0;
         while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
         if (p.G == 1 && (p.R << lg_nchp) <= 64)
-          merge_chunks_g1<D, NW>(p, b, h, s_nl, sh.m, lg_nchp);
+          merge_row_chunks<D, NW>(p, b, h, 0, 0, s_nl, sh.m, lg_nchp);
         else
           merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
       }
     }
   }
+}
+
+// The separate-launch step's chunk combine and cross-shard merge in one
+// kernel: one workgroup per (sequence b, query head), reading the chunk
+// partials and single-chunk shard results the attention launch wrote, and
+// writing o_part/lse_part of split shards and out/lse_out (merge_row_chunks).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void row_merge_kernel(const AttnParams kp) {
+  const void* ks_unused;
+  const void* vs_unused;
+  const Args p = load_args(kp, ks_unused, vs_unused);
+  __shared__ MergeSmem<NW, kStepOneChunks> ms;
+  __shared__ int s_nl[kMaxShards];
+  const int row = blockIdx.x;  // b * Hq + query head
+  const int b = row / p.Hq, hq = row - b * p.Hq;
+  const int h = hq / p.G, gl = hq - h * p.G;
+  const int gb = gl / kGroupRows, g = gl - gb * kGroupRows;
+  if (threadIdx.x < (unsigned)p.R) {
+    const int L = min(max(p.lens[threadIdx.x * p.B + b], 0), p.cap);
+    s_nl[threadIdx.x] = (L + p.chunk - 1) / p.chunk;
+  }
+  __syncthreads();
+  int lg_nchp = 0;
+  while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
+  merge_row_chunks<D, NW>(p, b, h, gb, g, s_nl, ms, lg_nchp);
 }
 
 // Merge the chunk partials of every unit that has more than one live chunk
@@ -1464,6 +1494,15 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
   hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (mode == kStepLaunches && p.nchunks >= 2) {  // chunk combine and merge in one launch
+    const dim3 rgrid((unsigned)((int64_t)p.B * p.Hq));
+    switch (row_merge_waves(p.R, p.nchunks, D)) {
+      case 2: hipLaunchKernelGGL((row_merge_kernel<D, 2>), rgrid, dim3(128), 0, s, p); return hipGetLastError();
+      case 4: hipLaunchKernelGGL((row_merge_kernel<D, 4>), rgrid, dim3(256), 0, s, p); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((row_merge_kernel<D, 8>), rgrid, dim3(512), 0, s, p); return hipGetLastError();
+      default: break;
+    }
+  }
   if (p.nchunks >= 2) {
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, p);
     e = hipGetLastError();

@@ -207,8 +207,14 @@ cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches) {
   AttnPlan pl;
   const cpdec_status st = plan_attn(d, &pl);
   if (st != CPDEC_OK) return st;
-  if (launches)
-    *launches = pl.step != kStepLaunches ? 1 : (pl.nchunks > 1 ? 3 : 2) + (pl.ordered ? 1 : 0);
+  if (launches) {
+    int n = 1;
+    if (pl.step == kStepLaunches) {
+      const bool row = row_merge_waves(d->num_shards, pl.nchunks, d->head_dim) > 0;
+      n = (pl.nchunks > 1 && !row ? 3 : 2) + (pl.ordered ? 1 : 0);
+    }
+    *launches = n;
+  }
   return CPDEC_OK;
 }
 

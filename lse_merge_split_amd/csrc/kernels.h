@@ -89,6 +89,22 @@ constexpr int64_t kStepUnsplitBlocks = 1024; // unsplit shards: one launch up to
 constexpr int kStepTwoLevelMaxChunks = 64;   // chunks per shard in the two-level form (lanes
                                              // of one wave per head in the chunk statistics)
 
+// Separate-launch step with split shards: when a query head's (shard, chunk)
+// pairs fit one wave (R * chunks rounded up to a power of two <= 64), one
+// kernel with a workgroup per (sequence, query head) combines the chunks and
+// merges the shards (instead of a chunk-combine and a merge launch).  Its
+// waves: threads >= max(R * D/4, D) (one (shard, float4) item per thread, and
+// every live chunk within the 16 loads per thread group).  0: not eligible.
+inline int row_merge_waves(int R, int nchunks, int D) {
+  int nchp = 1;
+  while (nchp < nchunks) nchp <<= 1;
+  if (nchunks < 2 || R * nchp > 64) return 0;
+  const int need = R * (D / 4) > D ? R * (D / 4) : D;
+  int w = 2;
+  while (w < 8 && 64 * w < need) w *= 2;
+  return 64 * w >= need ? w : 0;
+}
+
 // Launch the partial-attention kernel over (units / R) x nchunks x R workgroups and
 // whatever else `mode` needs (chunk combine and merge kernels for
 // kPartialsOnly/kStepLaunches; nothing for the one-launch modes).

@@ -69,19 +69,25 @@ def test_step_plan_launches():
     # 16 heads x 256/4 vectors per shard: more than one merging workgroup's threads
     wide = dict(num_q_heads=32, num_kv_heads=2, head_dim=256, kv_stride_token=256,
                 kv_stride_head=1000 * 256, kv_stride_batch=2 * 1000 * 256)
-    # split, 16 heads x 64 vectors beyond the workgroup: attention, combine, merge
-    assert cp.step_launches(_desc(chunk_tokens=128, **wide)) == 3
+    # split, 16 heads x 64 vectors beyond the workgroup: attention, then one kernel that
+    # combines the chunks and merges the shards per (sequence, query head)
+    assert cp.step_launches(_desc(chunk_tokens=128, **wide)) == 2
     # split, 4 heads x 32 vectors fit, 8 shards do not: two levels in the one launch
     # (chunk combine per unit, shard merge per group)
     assert cp.step_launches(_desc(chunk_tokens=128, num_shards=8)) == 1
     assert cp.step_launches(_desc(chunk_tokens=1024, **wide)) == 2  # attention, merge
-    # more than 16 chunks per shard: two levels; more than 64: attention, combine, merge
+    # more than 16 chunks per shard: two levels; more than 64 (shards x chunks beyond one
+    # wave): attention, combine, merge
     assert cp.step_launches(_desc(chunk_tokens=32)) == 1
     long = dict(kv_capacity=4096, kv_stride_head=4096 * 128, kv_stride_batch=2 * 4096 * 128)
     assert cp.step_launches(_desc(chunk_tokens=32, **long)) == 3
-    # two levels need a counter line per unit and per group (at most 1024 lines)
+    # two levels need a counter line per unit and per group (at most 1024 lines); beyond,
+    # attention + the per-row combine-and-merge kernel (8 shards x 8 chunks = one wave)
     many8 = dict(num_shards=8, batch=100, kv_stride_batch=2 * 1000 * 128)
-    assert cp.step_launches(_desc(chunk_tokens=128, **many8)) == 3
+    assert cp.step_launches(_desc(chunk_tokens=128, **many8)) == 2
+    many8_long = dict(many8, kv_capacity=2000, kv_stride_head=2000 * 128,
+                      kv_stride_batch=2 * 2000 * 128)
+    assert cp.step_launches(_desc(chunk_tokens=128, **many8_long)) == 3  # 8 x 16 chunks
     # more than 8 whole shards
     assert cp.step_launches(_desc(chunk_tokens=1024, num_shards=9)) == 2
     # more (sequence, kv head) groups than counters

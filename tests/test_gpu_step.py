@@ -30,16 +30,17 @@ CASES = {
     "c2": (sc.WORKLOADS["c2"], 0, 1),
     "c2 chunk 32 (128 chunks: separate launches)": (sc.WORKLOADS["c2"], 32, 3),
     "ragged GQA 8, B16": (sc.small("c4", B=16, Lcap=512), 0, 1),
-    "ragged GQA 8, B2 split (group too big: separate launches)": (sc.small("c4", B=2, Lcap=512), 0, 3),
+    "ragged GQA 8, B2 split (group too big: attention + row merge)": (sc.small("c4", B=2, Lcap=512), 0, 2),
     "ragged GQA 4, B2 split (two levels)": (sc.small("c4", B=2, Hq=32, Lcap=512), 0, 1),
     "ragged GQA 8, B1 split, 64 chunks (two levels)": (sc.small("c4", B=1, Lcap=2048), 32, 1),
     "ragged GQA 8, B1 split, 65 chunks (separate launches)": (sc.small("c4", B=1, Lcap=2080), 32, 3),
     "GQA 8 D64 B1 split, 32 chunks (two levels, two head passes)":
         (sc.small("c3", R=8, B=1, Hq=16, Hkv=2, D=64, Lcap=2048, L=2000), 0, 1),
     "ragged GQA 8, B64 (large unsplit grid)": (sc.small("c4", B=64, Lcap=512), 0, 2),
-    "D256 G20 (over the merging workgroup: separate launches)":
-        (sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290), 0, 3),
-    "fp16 GQA 8 split (separate launches)": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 3),
+    "D256 G20 (over the merging workgroup: attention + row merge)":
+        (sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290), 0, 2),
+    "ragged GQA 8, B2 split, 8 x 32 chunks (4 waves: two levels)": (sc.small("c4", B=2, Lcap=1024), 32, 1),
+    "fp16 GQA 8 split (attention + row merge)": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 2),
     "fp16 GQA 4 split (two levels)": (sc.small("c4", B=4, Hq=32, Lcap=256, dtype="fp16"), 0, 1),
     "fp16 GQA 2 split": (sc.small("c4", B=2, Hq=16, Lcap=256, dtype="fp16"), 0, 1),
     "D64 G3": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 0, 1),
