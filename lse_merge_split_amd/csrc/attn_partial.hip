@@ -350,8 +350,8 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
     const uint32_t span0 = rows_span(min(p.cap, t_begin + p.chunk));
     const rsrc_t k0 = make_rsrc(kb, span0), v0 = make_rsrc(vb, span0);
     load_tile(t0, k0, v0, kt0, vt0);
-    // SPEC2 (split shards with several tiles per wave): the second tile too is
-    // requested before the length is known, one memory round trip earlier.
+    // SPEC2 (split shards with two or more tiles per wave): the second tile too
+    // is requested before the length is known, one memory round trip earlier.
     if constexpr (SPEC2) load_tile(t0 + NW * kTileTokens, k0, v0, kt1, vt1);
   }
   if constexpr (kDev) {  // every shard's length of this sequence, for the merge (used at the end)
@@ -1491,7 +1491,10 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
       hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepTwoLevel>), grid, block, 0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);
+  if (p.nchunks >= 2 && p.chunk >= 2 * NW * kTileTokens)  // split, two or more tiles per wave
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly, false, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsOnly>), grid, block, 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mode == kStepLaunches && p.nchunks >= 2) {  // chunk combine and merge in one launch
@@ -1536,6 +1539,7 @@ hipError_t launch_d(const AttnParams& p, int D, int waves, int64_t units, StepMo
   return hipErrorInvalidValue;
 }
 
+#if !defined(CPDEC_ATTN_TYPE) || CPDEC_ATTN_TYPE == 2
 __global__ void clear_kernel(u32x4* p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
        i += (size_t)gridDim.x * blockDim.x)
@@ -1545,13 +1549,30 @@ __global__ void clear_kernel(u32x4* p, size_t n16) {
 __global__ void clear_tail_kernel(unsigned char* q, size_t n) {
   if (threadIdx.x < n) q[threadIdx.x] = 0;
 }
+#endif
 
 }  // namespace
 
+// The build compiles this file once per element type (CPDEC_ATTN_TYPE = 2:
+// bf16 with the type dispatch and the clear kernels, 1: fp16) into separate
+// objects, in parallel; without the macro the file holds everything.
+#if !defined(CPDEC_ATTN_TYPE) || CPDEC_ATTN_TYPE == 2
+hipError_t launch_attn_partial_bf16(const AttnParams& p, int D, int waves, int64_t units,
+                                    StepMode mode, hipStream_t s) {
+  return launch_d<bf16_t>(p, D, waves, units, mode, s);
+}
+#endif
+#if !defined(CPDEC_ATTN_TYPE) || CPDEC_ATTN_TYPE == 1
+hipError_t launch_attn_partial_f16(const AttnParams& p, int D, int waves, int64_t units,
+                                   StepMode mode, hipStream_t s) {
+  return launch_d<f16_t>(p, D, waves, units, mode, s);
+}
+#endif
+#if !defined(CPDEC_ATTN_TYPE) || CPDEC_ATTN_TYPE == 2
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves, int64_t units,
                                StepMode mode, hipStream_t s) {
-  if (qkv_dt == kBF16) return launch_d<bf16_t>(p, D, waves, units, mode, s);
-  if (qkv_dt == kF16) return launch_d<f16_t>(p, D, waves, units, mode, s);
+  if (qkv_dt == kBF16) return launch_attn_partial_bf16(p, D, waves, units, mode, s);
+  if (qkv_dt == kF16) return launch_attn_partial_f16(p, D, waves, units, mode, s);
   return hipErrorInvalidValue;
 }
 
@@ -1569,5 +1590,6 @@ hipError_t launch_clear(void* ptr, size_t bytes, hipStream_t s) {
                        static_cast<unsigned char*>(ptr) + n16 * 16, tail);
   return hipGetLastError();
 }
+#endif
 
 }  // namespace cpdec

@@ -110,6 +110,11 @@ inline int row_merge_waves(int R, int nchunks, int D) {
 // kPartialsOnly/kStepLaunches; nothing for the one-launch modes).
 hipError_t launch_attn_partial(const AttnParams& p, int qkv_dt, int D, int waves,
                                int64_t units, StepMode mode, hipStream_t s);
+// the same for one element type (the per-type halves of the build)
+hipError_t launch_attn_partial_bf16(const AttnParams& p, int D, int waves, int64_t units,
+                                    StepMode mode, hipStream_t s);
+hipError_t launch_attn_partial_f16(const AttnParams& p, int D, int waves, int64_t units,
+                                   StepMode mode, hipStream_t s);
 
 hipError_t launch_lse_merge(const void* o, const float* lse, int R, int64_t rows, int D,
                             int in_dt, int out_dt, void* out, float* lse_out, hipStream_t s);
