@@ -238,9 +238,12 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  * chunk workgroup of each (shard, sequence, kv head) combines its chunks,
  * the last of the group's shards merges them -- when min(G,16) x D/4 <= the
  * workgroup's threads, at most 64 chunks and units + groups <= 1024.
- * Otherwise the step runs as attention, chunk-merge and merge launches, where
- * the merge work spreads over many workgroups, with the order pre-pass of
- * cpdec_attn_order in front when it applies (cpdec_step_plan tells which).
+ * Otherwise the step runs as separate launches: the attention, then -- when a
+ * query head's shards x chunks (chunks rounded up to a power of two) are at
+ * most 64 -- one kernel that combines the chunks and merges the shards per
+ * (sequence, query head), else a chunk-combine and a merge launch; the order
+ * pre-pass of cpdec_attn_order goes in front when it applies (cpdec_step_plan
+ * tells how many launches).
  * `out` agrees with cpdec_lse_merge of the same partials to rounding.
  *
  *   d, q, k_shards, v_shards, lens, o_part, lse_part, stream
