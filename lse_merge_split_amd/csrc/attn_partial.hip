@@ -13,11 +13,13 @@
 //   A workgroup has NW waves; wave w takes the 32-token tiles w, w+NW, ... of
 //   its chunk and keeps an online-softmax state (running max m, exp-sum l,
 //   un-normalised accumulator) per query head, loading tile i+1 while it
-//   computes tile i.  The waves' states are merged through LDS.  A unit whose
-//   tokens fit one chunk is written straight to o_part/lse_part; otherwise each
-//   chunk writes a normalised partial to the workspace.  Every merge -- chunks
-//   of a shard, shards of a sequence -- uses the LSE weighting of the page's
-//   merge formula, which makes it exact.
+//   computes tile i (split shards: the first two tiles are requested before
+//   the length is known).  The waves' states are merged through LDS.  A unit
+//   whose tokens fit one chunk is written straight to o_part/lse_part;
+//   otherwise each chunk writes a normalised partial to the workspace.  Every
+//   merge -- chunks of a shard, shards of a sequence -- uses the LSE weighting
+//   of the page's merge formula, which makes it exact.  Large ragged grids of
+//   unsplit shards may take their units longest first (order_kernel).
 //
 // Who merges:
 //   * partials only (cpdec_attn_partial): a second, small kernel merges the
@@ -25,9 +27,16 @@
 //   * the whole step in one launch (cpdec_cp_decode): workgroups hand their
 //     results over with device-scope stores and an arrival counter per
 //     (sequence, kv head, head block); the workgroup that arrives last merges
-//     that group's chunks and shards.  No workgroup ever waits for another,
-//     and no device-scope fence is used: on gfx950 such a fence writes back
-//     and invalidates the XCD's L2, which costs microseconds per workgroup.
+//     that group's chunks and shards -- or, for split groups too big for one
+//     workgroup, in two levels: the last chunk of a unit combines the unit's
+//     chunks, the last unit of the group merges the shards.  No workgroup
+//     ever waits for another, and no device-scope fence is used: on gfx950
+//     such a fence writes back and invalidates the XCD's L2, which costs
+//     microseconds per workgroup.
+//   * the whole step as separate launches (groups beyond the one-launch
+//     limits): the attention, then one workgroup per (sequence, query head)
+//     combines and merges (row_merge_kernel), or the chunk-combine kernel and
+//     the merge kernel.
 //
 // Per 32-token tile, with G <= 16 query heads of one kv head as MFMA columns:
 //   S^T[t][g] = K[t][:] . Q[g][:]       4 (D/32) MFMA 16x16x32 per 16 tokens;
