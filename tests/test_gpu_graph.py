@@ -21,6 +21,8 @@ from synth import gpu as sg  # noqa: E402
     ("merge-only rows", None),
     ("one-launch step, split", sc.small("c4", B=2, Hq=8, Lcap=700)),
     ("one-launch step, whole shards", sc.small("c3", B=8, Lcap=640, L=600)),
+    ("one-launch step, two levels", sc.small("c4", B=2, Hq=32, Lcap=512)),
+    ("step as attention + row merge", sc.small("c4", B=2, Lcap=512)),
 ])
 def test_graph_replay_matches_eager(name, w):
     print(f"[case] graph replay: {name}", flush=True)
@@ -36,7 +38,7 @@ def test_graph_replay_matches_eager(name, w):
         cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
         refs = [ref_out, ref_lo]
         eager_work = lambda: cp.lse_merge(inp["o_part"], inp["lse_part"], ref_out, ref_lo)
-    elif name.startswith("one-launch step"):
+    elif "step" in name:
         inp = sg.attn_inputs(w)
         R, B, Hq, D = w.R, w.B, w.Hq, w.D
         mk = lambda: (torch.empty((R, B, Hq, D), dtype=torch.float32, device="cuda"),
@@ -44,7 +46,7 @@ def test_graph_replay_matches_eager(name, w):
                       torch.empty((B, Hq, D), dtype=inp["q"].dtype, device="cuda"),
                       torch.empty((B, Hq), dtype=torch.float32, device="cuda"))
         desc = cp.make_attn_desc(inp["q"], inp["k_shards"])
-        assert cp.step_launches(desc) == 1
+        assert cp.step_launches(desc) == (2 if "row merge" in name else 1)
         refs = list(mk())
         cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], *refs)
         outs = list(mk())

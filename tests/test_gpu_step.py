@@ -190,14 +190,16 @@ def test_step_padding_is_never_read():
 def test_step_16bit_partials(o_dt):
     """o_part stored in 16 bits: the merged output meets the bar against the
     storage-aware oracle (exact partials rounded to the storage type, then
-    merged exactly), on the one-launch split and unsplit forms."""
-    for name, w in (("split", sc.small("c4", B=2, Hq=16, Lcap=512)),
-                    ("split, two levels", sc.small("c4", B=2, Hq=32, Lcap=512)),
-                    ("unsplit", sc.small("c4", B=16, Lcap=512))):
+    merged exactly), in the one-launch split, two-level and unsplit forms and
+    the attention + row-merge form."""
+    for name, w, launches in (("split", sc.small("c4", B=2, Hq=16, Lcap=512), 1),
+                              ("split, two levels", sc.small("c4", B=2, Hq=32, Lcap=512), 1),
+                              ("split, attention + row merge", sc.small("c4", B=2, Lcap=512), 2),
+                              ("unsplit", sc.small("c4", B=16, Lcap=512), 1)):
         _say(f"step 16-bit partials {o_dt} {name}")
         inp = sg.attn_inputs(w)
         ws, desc = step_workspace(inp)
-        assert cp.step_launches(desc) == 1
+        assert cp.step_launches(desc) == launches
         res = run_step(inp, 0, ws, o_dtype=sg.torch_dtype(o_dt))
         for b in range(w.B):
             for h in range(w.Hkv):
