@@ -236,7 +236,14 @@ __device__ __forceinline__ Args load_args(const AttnParams& p, const void*& ksha
   a.chunk = p.chunk; a.nchunks = p.nchunks; a.units = p.units; a.odt = p.odt; a.out_dt = p.out_dt;
   a.cap = p.cap; a.scale_log2 = p.scale_log2;
   if constexpr (ORDERED) {  // the shard pointers come from the order entry instead
+    // (unsplit partials only: no workspace partials, no merge outputs, no counters)
     a.order = p.order;
+    a.ws_o = nullptr;
+    a.ws_lse = nullptr;
+    a.out = nullptr;
+    a.lse_out = nullptr;
+    a.counters = nullptr;
+    a.out_dt = 0;
     kshard = nullptr;
     vshard = nullptr;
     asm volatile(""
