@@ -43,6 +43,12 @@ CASES = {
     "fp16 GQA 8 split (attention + row merge)": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 2),
     "fp16 GQA 4 split (two levels)": (sc.small("c4", B=4, Hq=32, Lcap=256, dtype="fp16"), 0, 1),
     "fp16 GQA 2 split": (sc.small("c4", B=2, Hq=16, Lcap=256, dtype="fp16"), 0, 1),
+    "GQA 32 D64, two head blocks, chunk 256 (two levels)":
+        (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 256, 1),
+    "GQA 32 D64, two head blocks (attention, combine, merge)":
+        (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 0, 3),
+    "GQA 24, two head blocks (attention + row merge)":
+        (sc.small("c3", R=4, B=2, Hq=48, Hkv=2, D=128, Lcap=1024, L=1000), 0, 2),
     "D64 G3": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 0, 1),
     "D64 G3 chunk 32": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 32, 1),
     "D256 G2 split": (sc.small("c3", R=2, B=1, Hq=4, Hkv=2, D=256, Lcap=700, L=650), 0, 1),
