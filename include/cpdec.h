@@ -257,7 +257,10 @@ cpdec_status cpdec_lse_merge(const void* o_part, const float* lse_part,
  *              zero again, whatever the shape.  The rest is scratch.  Two calls
  *              that may run at the same time need separate workspaces.
  * Errors: as cpdec_attn_partial; INVALID_ARG for a NULL out; ALIGNMENT for a
- * misaligned out or lse_out; WORKSPACE for a missing or short workspace.
+ * misaligned out or lse_out; WORKSPACE for a missing or short workspace;
+ * UNSUPPORTED when the step needs separate launches and B x Hq x D x
+ * (o_part element bytes) or R x B x Hq x 4 reaches 2 GiB (the merge kernel's
+ * 32-bit offsets, as for cpdec_lse_merge).
  */
 cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
                              const void* const* k_shards,

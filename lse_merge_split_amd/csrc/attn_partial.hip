@@ -1515,7 +1515,9 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
   if (e != hipSuccess) return e;
   if (mode == kStepLaunches && p.nchunks >= 2) {  // chunk combine and merge in one launch
     const dim3 rgrid((unsigned)((int64_t)p.B * p.Hq));
-    switch (row_merge_waves(p.R, p.nchunks, D)) {
+    const int64_t ws_o_bytes = (int64_t)p.units * p.nchunks * p.Gb * D * 4;
+    const int64_t opart_bytes = (int64_t)p.R * p.B * p.Hq * D * (p.odt == kF32 ? 4 : 2);
+    switch (row_merge_waves(p.R, p.nchunks, D, ws_o_bytes, opart_bytes)) {
       case 2: hipLaunchKernelGGL((row_merge_kernel<D, 2>), rgrid, dim3(128), 0, s, p); return hipGetLastError();
       case 4: hipLaunchKernelGGL((row_merge_kernel<D, 4>), rgrid, dim3(256), 0, s, p); return hipGetLastError();
       case 8: hipLaunchKernelGGL((row_merge_kernel<D, 8>), rgrid, dim3(512), 0, s, p); return hipGetLastError();

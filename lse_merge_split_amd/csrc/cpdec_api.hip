@@ -210,7 +210,11 @@ cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches) {
   if (launches) {
     int n = 1;
     if (pl.step == kStepLaunches) {
-      const bool row = row_merge_waves(d->num_shards, pl.nchunks, d->head_dim) > 0;
+      const int64_t ws_o_bytes = pl.units * pl.nchunks * pl.Gb * (int64_t)d->head_dim * 4;
+      const int64_t opart_bytes = (int64_t)d->num_shards * d->batch * d->num_q_heads *
+                                  d->head_dim * (d->opart_dtype == CPDEC_F32 ? 4 : 2);
+      const bool row = row_merge_waves(d->num_shards, pl.nchunks, d->head_dim, ws_o_bytes,
+                                       opart_bytes) > 0;
       n = (pl.nchunks > 1 && !row ? 3 : 2) + (pl.ordered ? 1 : 0);
     }
     *launches = n;
@@ -287,6 +291,14 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
     return CPDEC_ERR_ALIGNMENT;
   for (int r = 0; r < d->num_shards; ++r)
     if (!aligned16(k_shards[r]) || !aligned16(v_shards[r])) return CPDEC_ERR_ALIGNMENT;
+  // The separate-launch step runs the merge kernel, which addresses each
+  // shard's o_part rows and the lse array with 32-bit offsets.
+  if (so != nullptr && pl.step == kStepLaunches) {
+    const uint64_t rows = (uint64_t)d->batch * d->num_q_heads;
+    if (rows * (uint64_t)d->head_dim * dtype_size(d->opart_dtype) >= (1ull << 31) ||
+        rows * (uint64_t)d->num_shards * 4 >= (1ull << 31))
+      return CPDEC_ERR_UNSUPPORTED;
+  }
   const size_t need = so != nullptr ? pl.step_ws_bytes : pl.ws_bytes;
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need ||

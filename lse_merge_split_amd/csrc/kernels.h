@@ -94,11 +94,14 @@ constexpr int kStepTwoLevelMaxChunks = 64;   // chunks per shard in the two-leve
 // kernel with a workgroup per (sequence, query head) combines the chunks and
 // merges the shards (instead of a chunk-combine and a merge launch).  Its
 // waves: threads >= max(R * D/4, D) (one (shard, float4) item per thread, and
-// every live chunk within the 16 loads per thread group).  0: not eligible.
-inline int row_merge_waves(int R, int nchunks, int D) {
+// every live chunk within the 16 loads per thread group).  The kernel uses
+// 32-bit buffer offsets: the chunk partials (ws_o_bytes) and o_part
+// (opart_bytes) must stay below 2 GiB.  0: not eligible.
+inline int row_merge_waves(int R, int nchunks, int D, int64_t ws_o_bytes, int64_t opart_bytes) {
   int nchp = 1;
   while (nchp < nchunks) nchp <<= 1;
   if (nchunks < 2 || R * nchp > 64) return 0;
+  if (ws_o_bytes >= (int64_t(1) << 31) || opart_bytes >= (int64_t(1) << 31)) return 0;
   const int need = R * (D / 4) > D ? R * (D / 4) : D;
   int w = 2;
   while (w < 8 && 64 * w < need) w *= 2;

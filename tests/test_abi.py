@@ -223,6 +223,17 @@ def test_cp_decode_errors():
     assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, None, 0, None) == WS
     assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, A, cp.STEP_COUNTER_BYTES - 1, None) == WS
     assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A, A + 16, cp.STEP_COUNTER_BYTES, None) == WS
+    # separate launches whose merge would need offsets past 2 GiB: 65536 x 64 rows x 128 x 4 B
+    huge = _desc(batch=65536, num_q_heads=64, num_kv_heads=8, kv_capacity=64, kv_stride_token=128,
+                 kv_stride_head=64 * 128, kv_stride_batch=8 * 64 * 128, chunk_tokens=64)
+    assert cp.step_launches(huge) == 2
+    n = cp.step_workspace_bytes(huge)
+    assert f(ctypes.byref(huge), A, ks, ks, A, A, A, A, A, A, n, None) == UNSUPPORTED
+    # the same rows in 16 bits fit
+    huge16 = _desc(batch=65536, num_q_heads=64, num_kv_heads=8, kv_capacity=64, kv_stride_token=128,
+                   kv_stride_head=64 * 128, kv_stride_batch=8 * 64 * 128, chunk_tokens=64)
+    huge16.opart_dtype = cp.BF16
+    assert cp.attn_plan(huge16)["num_chunks"] == 1
 
 
 @needs_cpu_host
