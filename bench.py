@@ -110,9 +110,8 @@ def build_attn_steps(w: sc.Workload, torch, cp, sg, fused: bool = True):
                 nchunks=steps[0][0].plan["num_chunks"], waves=steps[0][0].plan["waves"],
                 workspace_bytes=steps[0][0].workspace_bytes,
                 longest_first=steps[0][0].plan["longest_first"],
-                launches=(steps[0][0].launches if fused else
-                          (2 if steps[0][0].plan["num_chunks"] == 1 else 3)
-                          + int(steps[0][0].plan["longest_first"])))
+                attn_launches=steps[0][0].plan["launches"],
+                launches=(steps[0][0].launches if fused else steps[0][0].plan["launches"] + 1))
     return steps, alg_attn, alg_merge, info
 
 
@@ -373,9 +372,12 @@ def main():
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
                    "waves_per_workgroup": info.get("waves"),
                    "longest_first": info.get("longest_first"), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom_name + ("" if w.merge_only or fused
-                                                           or info.get("nchunks", 1) == 1
-                                                           else " + attn_combine_kernel")
+        "roofline": {"bound": "hbm", "kernel": dom_name + (" + attn_combine_kernel" if not fused
+                                                           and not w.merge_only
+                                                           and info.get("nchunks", 1) > 1
+                                                           and info.get("attn_launches", 1) >
+                                                           1 + int(bool(info.get("longest_first")))
+                                                           else "")
                      + (" + order_kernel" if info.get("longest_first") and not fused else ""),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -89,10 +89,13 @@ typedef struct cpdec_attn_desc {
  * cpdec_attn_partial itself.
  *
  * Workspace layout, shared by both attention entry points: the first
- * CPDEC_STEP_COUNTER_BYTES bytes hold cpdec_cp_decode's arrival counters and
- * are never written by cpdec_attn_partial; then either the chunk partials
+ * CPDEC_STEP_COUNTER_BYTES bytes hold arrival counters (cpdec_cp_decode's,
+ * and cpdec_attn_partial's when it combines chunks in its launch); they must
+ * be zero before the first call on a workspace (cpdec_workspace_clear, once)
+ * and every completed call leaves them zero.  Then either the chunk partials
  * (split shards) or the longest-first launch order (32 bytes per (shard,
- * sequence) pair; see cpdec_attn_order).
+ * sequence) pair; see cpdec_attn_order), whose contents on entry do not
+ * matter.
  */
 #define CPDEC_STEP_COUNTER_BYTES 65536
 size_t cpdec_attn_workspace_bytes(const cpdec_attn_desc* d);
@@ -143,6 +146,14 @@ cpdec_status cpdec_attn_plan(const cpdec_attn_desc* d, int32_t* chunk_tokens,
 cpdec_status cpdec_attn_order(const cpdec_attn_desc* d, int32_t* longest_first);
 
 /*
+ * Number of kernel launches cpdec_attn_partial makes for `d` (1 or 2: the
+ * order pre-pass, or a chunk-combine launch when the combine does not fit the
+ * attention launch).  `launches` may be NULL.  Errors: the descriptor checks
+ * of cpdec_attn_partial; the output is untouched on error.
+ */
+cpdec_status cpdec_attn_launches(const cpdec_attn_desc* d, int32_t* launches);
+
+/*
  * Per-shard decode attention (page section "Introduction").
  *
  * For every shard r, sequence b and query head hq, with L = lens[r*B + b] and
@@ -167,15 +178,20 @@ cpdec_status cpdec_attn_order(const cpdec_attn_desc* d, int32_t* longest_first);
  *   o_part       device, [R][B][Hq][D] contiguous, opart_dtype, 16-byte aligned
  *   lse_part     device, float [R][B][Hq]
  *   workspace    device, at least cpdec_attn_workspace_bytes(d) bytes,
- *                256-byte aligned; may be NULL when that size is 0.  Scratch
- *                for the split-KV chunk partials; its contents on entry do not
- *                matter (no clearing is needed, also when one buffer serves
- *                descriptors of different shapes), and the counter region at
- *                its start is left untouched.  The call enqueues the
- *                attention kernel, preceded by the order pre-pass when the
- *                launch is longest first (cpdec_attn_order) and followed by
- *                the merge of each shard's chunk partials when shards are
- *                split.
+ *                256-byte aligned; may be NULL when that size is 0.  Its
+ *                counter region (the first CPDEC_STEP_COUNTER_BYTES bytes)
+ *                must be zero before the first call on it and is left zero
+ *                by every completed call; the rest holds the split-KV chunk
+ *                partials or the launch order, and its contents on entry do
+ *                not matter (also when one buffer serves descriptors of
+ *                different shapes).  Two calls that may run at the same time
+ *                need separate workspaces.  When shards are split, the last
+ *                chunk workgroup of each (shard, sequence, kv head) combines
+ *                that unit's chunks in the attention launch (at most 64
+ *                chunks and 1024 such units); beyond that a chunk-combine
+ *                launch follows.  The order pre-pass precedes the attention
+ *                when the launch is longest first (cpdec_attn_order).
+ *                cpdec_attn_launches tells the count.
  *   stream       hipStream_t
  * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP (see above).
  */
@@ -271,10 +287,10 @@ cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
 
 /*
  * Zero-fill `bytes` bytes of a buffer on `stream` with a kernel (no
- * hipMemset, so it is safe to record in a HIP graph).  A new workspace for
- * cpdec_cp_decode needs it once (its counter region must start at zero);
- * cpdec_attn_partial needs no clearing.  `workspace` must be 256-byte
- * aligned.  Errors: INVALID_ARG, ALIGNMENT, HIP.
+ * hipMemset, so it is safe to record in a HIP graph).  A new workspace needs
+ * it once, for its counter region (the first CPDEC_STEP_COUNTER_BYTES bytes),
+ * before its first use by either attention entry point.  `workspace` must be
+ * 256-byte aligned.  Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 cpdec_status cpdec_workspace_clear(void* workspace, size_t bytes, void* stream);
 

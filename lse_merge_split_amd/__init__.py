@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.cpdec_attn_plan.restype = ctypes.c_int
         L.cpdec_attn_order.argtypes = [ctypes.POINTER(AttnDesc), pi]
         L.cpdec_attn_order.restype = ctypes.c_int
+        L.cpdec_attn_launches.argtypes = [ctypes.POINTER(AttnDesc), pi]
+        L.cpdec_attn_launches.restype = ctypes.c_int
         L.cpdec_attn_partial.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
         L.cpdec_attn_partial.restype = ctypes.c_int
@@ -129,7 +131,8 @@ def make_attn_desc(q, k_shards, *, kv_capacity=None, sm_scale=0.0, opart_dtype=N
 
 def attn_plan(desc: AttnDesc) -> dict:
     """The library's launch plan for a descriptor: chunk tokens, chunks, waves,
-    and whether the units are launched longest first."""
+    whether the units are launched longest first, and cpdec_attn_partial's
+    kernel launches."""
     c, n, wv, lf = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     rc = lib().cpdec_attn_plan(ctypes.byref(desc), ctypes.byref(c), ctypes.byref(n), ctypes.byref(wv))
     if rc != 0:
@@ -137,8 +140,12 @@ def attn_plan(desc: AttnDesc) -> dict:
     rc = lib().cpdec_attn_order(ctypes.byref(desc), ctypes.byref(lf))
     if rc != 0:
         raise CpdecError(rc, "cpdec_attn_order")
+    nl = ctypes.c_int32()
+    rc = lib().cpdec_attn_launches(ctypes.byref(desc), ctypes.byref(nl))
+    if rc != 0:
+        raise CpdecError(rc, "cpdec_attn_launches")
     return dict(chunk_tokens=c.value, num_chunks=n.value, waves=wv.value,
-                longest_first=bool(lf.value))
+                longest_first=bool(lf.value), launches=nl.value)
 
 
 def attn_workspace_bytes(desc: AttnDesc) -> int:
@@ -180,7 +187,10 @@ def _workspace(device, nbytes):
 class AttnCall:
     """A cpdec_attn_partial call with its arguments marshalled once.
 
-    Calling it enqueues the kernel on the current stream (or ``stream``)."""
+    Calling it enqueues the kernel(s) on the current stream (or ``stream``).
+    A workspace passed in must have its first STEP_COUNTER_BYTES bytes zero
+    before the first call (see workspace_clear); the binding's own workspaces
+    are zero-filled when allocated."""
 
     _workspace_query = staticmethod(attn_workspace_bytes)
 

@@ -126,7 +126,8 @@ struct Smem {
 // attention's LDS: it is used only after the workgroup's own chunk is done).
 template <int NW, int MODE>
 struct MergeSmem {
-  static constexpr bool kChunks = MODE == kStepOneChunks || MODE == kStepTwoLevel;
+  static constexpr bool kChunks =
+      MODE == kStepOneChunks || MODE == kStepTwoLevel || MODE == kPartialsCombine;
   float w[kChunks ? kStepSlots : 1];    // chunk weights, [(r * ng + g) * nchunks + c]
   f32x4 y[kChunks ? kStepVecs : 1];     // shard partials as stored, [r * E + e]
   f32x4 part[kChunks ? NW * 64 : 1];    // partition sums
@@ -1262,7 +1263,13 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     wait_vm_all();
     __syncthreads();
     const int grp = (b * p.Hkv + h) * p.gblocks + gb;
-    if constexpr (MODE == kStepTwoLevel) {
+    if constexpr (MODE == kPartialsCombine) {
+      // Partials only: the unit's last chunk workgroup combines its chunks.
+      if (threadIdx.x == 0) s_last = arrive(p.counters + unit * kStepCounterStride, p.nchunks);
+      __syncthreads();
+      if (!s_last) return;
+      combine_unit<D, NW>(p, unit, r, b, h, gb, s_nl[r], sh.m);
+    } else if constexpr (MODE == kStepTwoLevel) {
       // Level 1: the unit's chunk workgroups (counter line `unit`); the last
       // one combines the unit's chunks into o_part/lse_part.
       if (threadIdx.x == 0) s_last = arrive(p.counters + unit * kStepCounterStride, p.nchunks);
@@ -1497,6 +1504,14 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
                          s, p);
     else
       hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  if (mode == kPartialsCombine) {
+    if (p.chunk >= 2 * NW * kTileTokens)
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsCombine, false, true>), grid, block,
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kPartialsCombine>), grid, block, 0, s, p);
     return hipGetLastError();
   }
   if (mode == kStepTwoLevel) {

@@ -59,6 +59,7 @@ struct AttnPlan {
   size_t off_lse = 0, off_o = 0;
   size_t off_order = 0;      // longest-first launch order entries (when ordered)
   bool ordered = false;      // launch (shard, sequence) pairs longest first
+  bool partials_combine = false;  // cpdec_attn_partial combines chunks in its one launch
   StepMode step = kStepLaunches;  // how cpdec_cp_decode runs
 };
 
@@ -168,6 +169,12 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   p.step = one ? (p.nchunks > 1 ? kStepOneChunks : kStepOneShards)
                : (two ? kStepTwoLevel : kStepLaunches);
 
+  // cpdec_attn_partial with split shards: the unit's last chunk workgroup
+  // combines the chunks in the attention launch (one counter line per unit).
+  p.partials_combine = p.nchunks > 1 && !overrides().step_launches && p.units <= kStepCounters &&
+                       p.nchunks <= kStepTwoLevelMaxChunks && opart_bytes < (1ull << 31) &&
+                       slots * (size_t)D * sizeof(float) < (1ull << 31);
+
   // Longest-first launch order for large grids of unsplit shards when the
   // library picks the schedule: the order entries follow the counter region.
   // (Such grids never take the one-launch step: kOrderMinUnits > kStepUnsplitBlocks.)
@@ -219,6 +226,15 @@ cpdec_status cpdec_step_plan(const cpdec_attn_desc* d, int32_t* launches) {
     }
     *launches = n;
   }
+  return CPDEC_OK;
+}
+
+cpdec_status cpdec_attn_launches(const cpdec_attn_desc* d, int32_t* launches) {
+  AttnPlan pl;
+  const cpdec_status st = plan_attn(d, &pl);
+  if (st != CPDEC_OK) return st;
+  if (launches)
+    *launches = 1 + (pl.ordered ? 1 : 0) + (pl.nchunks > 1 && !pl.partials_combine ? 1 : 0);
   return CPDEC_OK;
 }
 
@@ -323,6 +339,10 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
   }
   if (pl.ordered) p.order = static_cast<char*>(workspace) + pl.off_order;
   StepMode mode = kPartialsOnly;
+  if (so == nullptr && pl.partials_combine) {
+    mode = kPartialsCombine;
+    p.counters = static_cast<int32_t*>(workspace);
+  }
   if (so != nullptr) {
     mode = pl.step;
     p.out = so->out;

@@ -69,6 +69,8 @@ enum StepMode : int {
                        // for one merging workgroup: the last chunk workgroup of
                        // a unit combines its chunks, the last unit of a group
                        // merges the shards
+  kPartialsCombine = 5,  // cpdec_attn_partial, shards split: the last chunk
+                         // workgroup of a unit combines its chunks in the launch
 };
 
 // Limits of the one-launch step.  The workgroup that merges a group fetches

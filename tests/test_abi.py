@@ -99,6 +99,27 @@ def test_step_plan_launches():
     assert cp.lib().cpdec_step_plan(None, None) == INVALID
 
 
+def _attn_launches(d):
+    n = ctypes.c_int32(-1)
+    rc = cp.lib().cpdec_attn_launches(ctypes.byref(d), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_attn_partial_launches():
+    """cpdec_attn_partial: one launch, the chunk combine inside it when shards
+    are split (at most 64 chunks, 1024 units); a combine launch beyond."""
+    assert _attn_launches(_desc(chunk_tokens=1024)) == (OK, 1)   # one chunk
+    assert _attn_launches(_desc(chunk_tokens=128)) == (OK, 1)    # 8 chunks, combined in the launch
+    long = dict(kv_capacity=4096, kv_stride_head=4096 * 128, kv_stride_batch=2 * 4096 * 128)
+    assert _attn_launches(_desc(chunk_tokens=64, **long)) == (OK, 1)   # 64 chunks
+    assert _attn_launches(_desc(chunk_tokens=32, **long)) == (OK, 2)   # 128 chunks: combine launch
+    many = dict(batch=200, kv_stride_batch=2 * 1000 * 128)              # 4 x 200 x 2 = 1600 units
+    assert _attn_launches(_desc(chunk_tokens=128, **many)) == (OK, 2)
+    assert cp.attn_plan(_desc(chunk_tokens=128))["launches"] == 1
+    assert _attn_launches(_desc(head_dim=96)) == (UNSUPPORTED, -1)
+    assert cp.lib().cpdec_attn_launches(None, None) == INVALID
+
+
 def _order(d):
     lf = ctypes.c_int32(-1)
     rc = cp.lib().cpdec_attn_order(ctypes.byref(d), ctypes.byref(lf))
@@ -120,6 +141,7 @@ def test_longest_first_order_plan():
     assert lib.cpdec_attn_workspace_bytes(ctypes.byref(d)) == C + 8 * 64 * 32
     assert lib.cpdec_step_workspace_bytes(ctypes.byref(d)) == C + 8 * 64 * 32
     assert cp.step_launches(d) == 3  # order pre-pass, attention, merge
+    assert _attn_launches(d) == (OK, 2)  # order pre-pass, attention
     # an explicit chunk length fixes the schedule: index order, no workspace
     fixed = _desc(chunk_tokens=8192, **big)
     assert _order(fixed) == (OK, 0)

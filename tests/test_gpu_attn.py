@@ -145,8 +145,9 @@ def test_attn_workspace_reuse_and_determinism():
 
 
 def test_attn_workspace_contents_do_not_matter():
-    """A workspace full of random bytes, or one last used by a different
-    shape, gives the same bits as a fresh one."""
+    """A workspace full of random bytes past its counter region, or one last
+    used by a different shape, gives the same bits as a fresh one, and every
+    call leaves the counter region zero."""
     w = SMALL["c4_small"]
     _say("attn garbage / cross-shape workspace")
     inp = sg.attn_inputs(w)
@@ -154,8 +155,10 @@ def test_attn_workspace_contents_do_not_matter():
     nb = cp.attn_workspace_bytes(desc)
     ws = torch.zeros(nb + (1 << 20), dtype=torch.uint8, device="cuda")
     ref = run_path(inp, chunk_tokens=64, workspace=ws)
-    ws.random_(0, 256)
+    C = cp.STEP_COUNTER_BYTES
+    ws[C:].random_(0, 256)
     got = run_path(inp, chunk_tokens=64, workspace=ws)
+    assert int(torch.count_nonzero(ws[:C]).item()) == 0
     for key in ref:
         assert torch.equal(ref[key], got[key]), key
     # another shape writes its partials over this shape's slot region, then back
@@ -165,6 +168,7 @@ def test_attn_workspace_contents_do_not_matter():
     again = run_path(inp, chunk_tokens=64, workspace=ws)
     for key in ref:
         assert torch.equal(ref[key], again[key]), key
+    assert int(torch.count_nonzero(ws[:C]).item()) == 0
     check_groups(w, inp, again, all_groups(w))
 
 

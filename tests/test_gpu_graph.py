@@ -63,8 +63,8 @@ def test_graph_replay_matches_eager(name, w):
         lse_part = torch.empty((R, B, Hq), dtype=torch.float32, device="cuda")
         out = torch.empty((B, Hq, D), dtype=inp["q"].dtype, device="cuda")
         lo = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(256, cp.attn_workspace_bytes(cp.make_attn_desc(inp["q"], inp["k_shards"]))),
-                         dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(256, cp.attn_workspace_bytes(cp.make_attn_desc(inp["q"], inp["k_shards"]))),
+                         dtype=torch.uint8, device="cuda")  # counter region zero before the first call
         calls = [cp.AttnCall(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], o_part, lse_part,
                              workspace=ws),
                  cp.MergeCall(o_part, lse_part, out, lo)]
