@@ -170,13 +170,18 @@ def step_launches(desc: AttnDesc) -> int:
 _WS_CACHE: dict = {}
 
 
-def _workspace(device, nbytes):
-    """A workspace of at least nbytes, reused across calls and shapes.  It is
-    zero-filled when allocated: cpdec_cp_decode needs its counter region to
-    start at zero, and every call leaves it zero (cpdec_attn_partial never
-    writes it)."""
+def _workspace(device, nbytes, stream=None):
+    """A workspace of at least nbytes, reused across calls and shapes on the
+    current stream of `device` (one per stream: calls on different streams
+    may overlap and must not share one).  It is zero-filled when allocated:
+    both attention entry points need its counter region to start at zero,
+    and every completed call leaves it zero.  Calls marshalled once
+    (AttnCall, StepCall) keep the workspace of the stream current when they
+    were made."""
     torch = _torch()
-    key = (str(device),)
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    key = (str(device), stream)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -189,13 +194,15 @@ class AttnCall:
 
     Calling it enqueues the kernel(s) on the current stream (or ``stream``).
     A workspace passed in must have its first STEP_COUNTER_BYTES bytes zero
-    before the first call (see workspace_clear); the binding's own workspaces
-    are zero-filled when allocated."""
+    before the first call (see workspace_clear); without one, the binding
+    picks its zero-filled workspace of the stream given as ``stream`` here
+    (default: the current stream), so calls made for different streams never
+    share one."""
 
     _workspace_query = staticmethod(attn_workspace_bytes)
 
     def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
-                 kv_capacity=None, workspace=None, chunk_tokens=0):
+                 kv_capacity=None, workspace=None, chunk_tokens=0, stream=None):
         torch = _torch()
         if len(k_shards) != len(v_shards):
             raise ValueError("k_shards and v_shards differ in length")
@@ -218,7 +225,7 @@ class AttnCall:
         self.workspace_bytes = self._workspace_query(desc)
         self.plan = attn_plan(desc)
         if workspace is None and self.workspace_bytes > 0:
-            workspace = _workspace(q.device, self.workspace_bytes)
+            workspace = _workspace(q.device, self.workspace_bytes, _stream_handle(stream))
         self._keep = (q, list(k_shards), list(v_shards), lens, o_part, lse_part, workspace)
         self.desc = desc
         self._device = q.device
@@ -272,7 +279,7 @@ class StepCall(AttnCall):
 def cp_decode(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, *, stream=None,
               **kw):
     """Whole step: per-shard partials into o_part/lse_part and their merge into out/lse_out."""
-    StepCall(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out, **kw)(
+    StepCall(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out, stream=stream, **kw)(
         _stream_handle(stream))
 
 
@@ -313,8 +320,8 @@ def attn_partial(q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
 
     lens: int32 device tensor [R, B]."""
     AttnCall(q, k_shards, v_shards, lens, o_part, lse_part, sm_scale=sm_scale,
-             kv_capacity=kv_capacity, workspace=workspace, chunk_tokens=chunk_tokens)(
-                 _stream_handle(stream))
+             kv_capacity=kv_capacity, workspace=workspace, chunk_tokens=chunk_tokens,
+             stream=stream)(_stream_handle(stream))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, *, stream=None):

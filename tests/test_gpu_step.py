@@ -221,3 +221,32 @@ def test_step_16bit_partials(o_dt):
                                for g in range(w.G)])
                 assert_out(to64(res["out"][b, hs]), sa, f"out vs storage-aware oracle b={b} h={h}")
                 assert_out(to64(res["o_part"][:, b, hs]), ref["o_part"], f"o_part b={b} h={h}")
+
+
+def test_step_on_two_streams_with_binding_workspaces():
+    """Calls made for two streams take the binding's workspace of their own
+    stream, so they may overlap: repeated interleaved enqueues on two streams
+    give the single-stream results bit for bit, and both counter regions end
+    at zero."""
+    _say("step on two streams")
+    wa, wb = sc.WORKLOADS["c1"], sc.small("c4", B=2, Hq=16, Lcap=512)
+    ia, ib = sg.attn_inputs(wa), sg.attn_inputs(wb)
+    ref_a, ref_b = run_step(ia), run_step(ib)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = {}
+    calls = {}
+    for name, inp, ref, s in (("a", ia, ref_a, sa), ("b", ib, ref_b, sb)):
+        res = {k: torch.empty_like(v) for k, v in ref.items()}
+        outs[name] = res
+        calls[name] = cp.StepCall(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"],
+                                  res["o_part"], res["lse_part"], res["out"], res["lse_out"], stream=s)
+    assert calls["a"]._keep[6].data_ptr() != calls["b"]._keep[6].data_ptr()
+    torch.cuda.synchronize()
+    for _ in range(20):
+        calls["a"](sa.cuda_stream)
+        calls["b"](sb.cuda_stream)
+    torch.cuda.synchronize()
+    for name, ref in (("a", ref_a), ("b", ref_b)):
+        for k in ref:
+            assert torch.equal(outs[name][k], ref[k]), f"stream {name}: {k} differs"
+        assert counters_zero(calls[name]._keep[6])
