@@ -106,14 +106,6 @@ __device__ __forceinline__ void store4(void* base, int64_t idx, f32x4 x, int odt
   }
 }
 
-// Load 4 consecutive values of dtype `odt` as fp32.
-__device__ __forceinline__ f32x4 load4(const void* base, int64_t idx, int odt) {
-  if (odt == kF32) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
-  const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + idx);
-  if (odt == kBF16) return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-  return f32x4{f16_lo(w[0]), f16_hi(w[0]), f16_lo(w[1]), f16_hi(w[1])};
-}
-
 template <int D, int NW>
 struct Smem {
   static constexpr int NB = (D / 8 + 15) / 16;
@@ -1252,7 +1244,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
     const int64_t orow0 = ((int64_t)r * p.B + b) * p.Hq + h * p.G + g0;
     for (int e = threadIdx.x; e < ng * (D / 4); e += NW * 64)
       store4(p.o_part, orow0 * D + 4 * e, f32x4{0.f, 0.f, 0.f, 0.f}, p.odt);
-    if (threadIdx.x < ng) p.lse_part[orow0 + threadIdx.x] = neg_inf();
+    if ((int)threadIdx.x < ng) p.lse_part[orow0 + threadIdx.x] = neg_inf();
   }
   if constexpr (MODE >= kStepOneShards) {
     // Arrival: this workgroup's device-scope stores are complete before the

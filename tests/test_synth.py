@@ -1,6 +1,5 @@
 """The seeded input streams (CPU side): generator known answers, rounding,
 distribution sanity and the workload recipes."""
-import math
 import os
 
 import numpy as np
