@@ -79,7 +79,13 @@ typedef struct cpdec_attn_desc {
   cpdec_dtype opart_dtype;/* o_part storage: CPDEC_F32 (recommended), F16,
                              BF16                                           */
   int32_t chunk_tokens;   /* split-KV chunk length in tokens; 0 lets the
-                             library pick, otherwise a multiple of 32       */
+                             library pick, otherwise a multiple of 32.  A
+                             request is raised to keep at most 256 chunks
+                             and lowered to at most 2^18 tokens (each wave
+                             accumulates its p.V sums in FP32; longer
+                             chunks drift past the output tolerance on
+                             inputs where one early token dominates);
+                             cpdec_attn_plan reports the length used      */
 } cpdec_attn_desc;
 
 /*

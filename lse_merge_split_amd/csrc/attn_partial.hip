@@ -313,7 +313,11 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
   const int64_t st = p.st;
 
   float m = neg_inf();  // running max (base-2 units), uniform over q4
-  float lsum = 0.f;     // this lane's share of the exp-sum
+  // This lane's share of the exp-sum, accumulated in FP64: after a dominant
+  // token the running sum sits near 1 while each tile adds a nearly constant
+  // small term, and FP32 round-to-nearest would then drop the same fraction of
+  // every term (an lse bias growing with the chunk length).
+  double lsum_d = 0.0;
   f32x4 acc[NB][8];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -413,7 +417,7 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_ref);
       float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      lsum = lsum * alpha + ps;
+      lsum_d = __builtin_fma(lsum_d, (double)alpha, (double)ps);
 
       // A tile crossing the end: V rows past it (padding read by the first,
       // speculative load) become zeros, since 0 * NaN would poison the sums.
@@ -485,6 +489,7 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
   }
   if (t_begin >= L) return false;  // empty chunk: nothing is written
 
+  float lsum = (float)lsum_d;
   {
     const f32x2 a = rows16(lsum);
     lsum = a[0] + a[1];

@@ -47,6 +47,15 @@ constexpr int kDefaultWaves = 4;        // waves per workgroup when shards are n
 constexpr int kSplitWaves = 2;          // waves per workgroup when shards are split
 constexpr int64_t kSplitBlocks = 512;   // fewer units than this: split shards into chunks,
                                         // aiming at this many workgroups
+// Longest chunk the library picks.  A wave accumulates its p.V sums in FP32
+// (MFMA accumulators), one rounding per tile; when one early token dominates
+// and the rest add nearly constant small terms, that rounding is biased, so
+// the error grows with the tiles per wave (measured on such input: ~1e-3 of
+// the output at 65536 tiles per wave, just past the output tolerance).  No
+// chunk is longer than 2^18 tokens, whoever picks it: a wave then sees at
+// most 2048 tiles in a 4-wave workgroup (4096 in a 2-wave one).  Longer
+// shards are split into chunks and merged with the LSE weighting.
+constexpr int kMaxChunkTokens = 1 << 18;
 
 struct AttnPlan {
   int waves = 0;
@@ -110,6 +119,7 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
     if (want > most) want = most;
     chunk = (int)(ceil_div(ceil_div(cap, want), span) * span);
   }
+  if (chunk > kMaxChunkTokens) chunk = kMaxChunkTokens;  // a multiple of every span
   if (ceil_div(cap, chunk) > kMaxChunks)
     chunk = (int)ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
   p.chunk = chunk;

@@ -310,3 +310,106 @@ def test_attn_full_c4():
         empty_b = int(np.where((lens == 0).any(axis=0))[0][-1])
         return [(0, 0), (11, 3), (12, 7), (empty_b, 2)]
     _full("c4", groups)
+
+
+# ------------------------------------------------------------ maximum capacity
+# The largest capacity the ABI accepts at D = 128, 16-bit K/V: one (shard,
+# sequence, kv head) spans just under 2 GiB (capacity * token stride * 2 <
+# 2^31, the limit of 32-bit buffer offsets).  The oracle cannot hold such
+# shards in float64, so the inputs have a closed-form result: ordinary tokens
+# have k = 0 and v = c; token 0 has k = b e_1 and v = vf, the last valid token
+# k = b e_0 and v = vl; query head 0 is a e_0 and head 1 a e_1.  With
+# E = exp(a b / sqrt(D)), head 0 gets o = (E vl + vf + (L-2) c) / (E + L - 1)
+# and head 1 o = (E vf + vl + (L-2) c) / (E + L - 1), both with
+# lse = ln(E + L - 1).  E is close to L, so the last token, the first and
+# every chunk of ordinary tokens all move the result.
+MAX_D = 128
+MAX_CAP = (2 ** 31 - 1) // (MAX_D * 2)          # 8,388,607 tokens
+
+
+def _max_cap_case():
+    a, bk = 12.0, 15.0                            # bf16-exact; a * bk / sqrt(128) = 15.91
+    R, cap, D = 2, MAX_CAP, MAX_D
+    lens = [cap, cap - 13]                        # full, and a ragged tail before NaN padding
+    d = torch.arange(1, D + 1, dtype=torch.float64)
+    vl = [d / 128, -d / 128]                      # per shard, bf16-exact
+    vf = [-d / 256, -d / 512]
+    c = [0.25, -0.125]
+    q = torch.zeros(1, 2, D, dtype=torch.bfloat16, device="cuda")
+    q[0, 0, 0], q[0, 1, 1] = a, a
+    ks, vs = [], []
+    for r in range(R):
+        L = lens[r]
+        k = torch.zeros(1, 1, cap, D, dtype=torch.bfloat16, device="cuda")
+        v = torch.full((1, 1, cap, D), c[r], dtype=torch.bfloat16, device="cuda")
+        k[0, 0, 0, 1] = bk
+        k[0, 0, L - 1, 0] = bk
+        v[0, 0, 0] = vf[r].to(torch.bfloat16).cuda()
+        v[0, 0, L - 1] = vl[r].to(torch.bfloat16).cuda()
+        if L < cap:                               # padding past the length: NaN, never read
+            k[0, 0, L:] = float("nan")
+            v[0, 0, L:] = float("nan")
+        ks.append(k)
+        vs.append(v)
+    E = np.exp(a * bk / np.sqrt(D))
+    o_ref = np.zeros((R, 1, 2, D))
+    o_mag = np.zeros((R, 1, 2, D))                # the same sums over |terms|
+    lse_ref = np.zeros((R, 1, 2))
+    for r in range(R):
+        L = lens[r]
+        den = E + (L - 1)
+        first, last = vf[r].numpy(), vl[r].numpy()
+        o_ref[r, 0, 0] = (E * last + first + (L - 2) * c[r]) / den
+        o_ref[r, 0, 1] = (E * first + last + (L - 2) * c[r]) / den
+        o_mag[r, 0, 0] = (E * np.abs(last) + np.abs(first) + (L - 2) * abs(c[r])) / den
+        o_mag[r, 0, 1] = (E * np.abs(first) + np.abs(last) + (L - 2) * abs(c[r])) / den
+        lse_ref[r, 0, :] = np.log(den)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda").view(R, 1)
+    return dict(q=q, k_shards=ks, v_shards=vs, lens=lens_t), o_ref, o_mag, lse_ref
+
+
+@pytest.mark.parametrize("chunk", [0, 2 ** 18, 2 ** 23],
+                         ids=["library chunks", "longest chunks", "whole shard asked, 2^18 used"])
+def test_attn_max_capacity(chunk):
+    """Both attention entry points at the largest capacity.  Per-shard
+    results against the magnitude of their terms: the FP32 p.V accumulation
+    drifts by ~1e-7 of it per tile a wave adds on this input (~5e-5 at the
+    library's 32K-token chunks, 512 tiles per wave; ~2e-4 at 2^18-token
+    chunks, 2048 tiles), while dropping one chunk would move the results by
+    ~1e-3 (32K tokens) or ~8e-3 (2^18 tokens).  A request for whole-shard
+    chunks gets the longest chunk the library runs, 2^18 tokens: over the
+    65536 tiles per wave of a whole shard the drift passes the output
+    tolerance on this input."""
+    from oracle import oracle as orc
+    _say(f"attn max capacity {MAX_CAP} tokens, chunk_tokens={chunk}: filling inputs")
+    inp, o_ref, o_mag, lse_ref = _max_cap_case()
+    desc = cp.make_attn_desc(inp["q"], inp["k_shards"], chunk_tokens=chunk)
+    plan = cp.attn_plan(desc)
+    assert plan["chunk_tokens"] == (min(chunk, 2 ** 18) if chunk else 32768)
+    over = cp.make_attn_desc(inp["q"], inp["k_shards"], kv_capacity=MAX_CAP + 1, chunk_tokens=chunk)
+    with pytest.raises(cp.CpdecError):            # one token more is past the 32-bit offsets
+        cp.attn_plan(over)
+    torch.cuda.synchronize()
+    _say(f"attn max capacity: plan {plan}, step launches {cp.step_launches(desc)}: two calls")
+    two = run_path(inp, chunk_tokens=chunk)
+    _say("attn max capacity: whole step")
+    ws = torch.zeros(cp.step_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    step = {k: torch.empty_like(t) for k, t in two.items()}
+    cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], step["o_part"],
+                 step["lse_part"], step["out"], step["lse_out"], chunk_tokens=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:cp.STEP_COUNTER_BYTES]).item()) == 0
+    out_ref = np.zeros((1, 2, MAX_D))
+    lo_ref = np.zeros((1, 2))
+    for h in range(2):
+        out_ref[0, h], lo_ref[0, h] = orc.merge(o_ref[:, 0, h], lse_ref[:, 0, h])
+    for what, res in (("two calls", two), ("step", step)):
+        o = to64(res["o_part"])
+        err = np.abs(o - o_ref) / o_mag
+        tol = 1e-4 if chunk == 0 else 5e-4
+        assert err.max() <= tol, f"{what} o_part: max error / term magnitude {err.max():.2e}"
+        assert_lse(to64(res["lse_part"]), lse_ref, f"{what} lse_part")
+        assert_out(to64(res["out"]), out_ref, f"{what} out")
+        assert_lse(to64(res["lse_out"]), lo_ref, f"{what} lse_out")
+    del inp, two, step, ws
+    torch.cuda.empty_cache()

@@ -23,14 +23,14 @@ def _desc(rng):
     G = int(rng.choice([1, 2, 4, 8, 16, 20, 32]))
     B = int(rng.choice([1, 2, 3, 8, 64, 256, 1000]))
     R = int(rng.choice([1, 2, 4, 8, 9, 16, 64]))
-    cap = int(rng.choice([1, 31, 32, 100, 512, 4096, 16384]))
+    cap = int(rng.choice([1, 31, 32, 100, 512, 4096, 16384, 300000, 1 << 20]))
     d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim, d.num_shards = B, G * Hkv, Hkv, D, R
     d.kv_capacity = cap
     d.kv_stride_token, d.kv_stride_head, d.kv_stride_batch = D, cap * D, Hkv * cap * D
     d.sm_scale = 0.0
     d.qkv_dtype = int(rng.choice([cp.BF16, cp.F16]))
     d.opart_dtype = int(rng.choice([cp.F32, cp.F32, cp.BF16]))
-    d.chunk_tokens = int(rng.choice([0, 0, 0, 32, 64, 256, 4096]))
+    d.chunk_tokens = int(rng.choice([0, 0, 0, 32, 64, 256, 4096, 1 << 21]))
     return d
 
 
@@ -58,8 +58,13 @@ def test_plan_invariants(seed):
         assert chunk % 32 == 0 and chunk > 0
         assert nch * chunk >= cap and (nch - 1) * chunk < cap
         assert waves in (1, 2, 4, 8)
-        if d.chunk_tokens:
-            assert chunk == d.chunk_tokens or nch == 256
+        assert nch <= 256
+        assert chunk <= 1 << 18  # short enough for the FP32 p.V accumulation
+        if d.chunk_tokens:  # as given, unless that makes more than 256 chunks
+            if -(-cap // d.chunk_tokens) <= 256:
+                assert chunk == min(d.chunk_tokens, 1 << 18)
+            else:           # then the fewest whole tiles that give at most 256
+                assert chunk == -(-(-(-cap // 256)) // 32) * 32
         # workspace: counters first, then what the plan writes
         ws_attn = lib.cpdec_attn_workspace_bytes(ctypes.byref(d))
         ws_step = lib.cpdec_step_workspace_bytes(ctypes.byref(d))
