@@ -413,3 +413,50 @@ def test_attn_max_capacity(chunk):
         assert_lse(to64(res["lse_out"]), lo_ref, f"{what} lse_out")
     del inp, two, step, ws
     torch.cuda.empty_cache()
+
+
+def test_attn_attention_sink():
+    """Token 0 of every (shard, sequence, kv head) carries about half of the
+    softmax weight (its key is the least-norm key that gives every query head
+    of the group the score 10.5, against ~N(0,1) for the other tokens): the
+    pattern under which FP32 running sums lose a fixed fraction of every
+    later term.  Ragged lengths up to 20000 tokens, both entry points, every
+    output against the oracle."""
+    from oracle import oracle as orc
+    R, B, Hq, Hkv, D, cap = 2, 2, 8, 2, 128, 20000
+    G = Hq // Hkv
+    lens = np.array([[20000, 15000], [17001, 20000]], np.int32)
+    _say("attention sink: inputs")
+    g = torch.Generator().manual_seed(4242)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(R, B, Hkv, cap, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(R, B, Hkv, cap, D, generator=g).to(torch.bfloat16)
+    Q = q.double().view(B, Hkv, G, D)
+    rhs = torch.full((B, Hkv, G, 1), 10.5 * np.sqrt(D), dtype=torch.float64)
+    sink = (Q.transpose(-1, -2) @ torch.linalg.solve(Q @ Q.transpose(-1, -2), rhs)).squeeze(-1)
+    k[:, :, :, 0] = sink.to(torch.bfloat16).unsqueeze(0)            # same key in every shard
+    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
+    o_ref, lp_ref, out_ref, lo_ref = orc.cp_decode(q64, list(k64), list(v64), lens, Hkv)
+    # the sink's share of the weight, from the oracle's own lse
+    s0 = np.einsum("bhgd,rbhd->rbhg", q64.reshape(B, Hkv, G, D), k64[:, :, :, 0]) / np.sqrt(D)
+    share = np.exp(s0.reshape(R, B, Hq) - lp_ref)
+    assert 0.3 < share.min() and share.max() < 0.8, f"sink share {share.min():.2f}..{share.max():.2f}"
+    inp = dict(q=q.cuda(), k_shards=[t.cuda() for t in k], v_shards=[t.cuda() for t in v],
+               lens=torch.from_numpy(lens).cuda())
+    _say("attention sink: two calls")
+    two = run_path(inp)
+    _say("attention sink: whole step")
+    desc = cp.make_attn_desc(inp["q"], inp["k_shards"])
+    ws = torch.zeros(cp.step_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    step = {kk: torch.empty_like(t) for kk, t in two.items()}
+    cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], step["o_part"],
+                 step["lse_part"], step["out"], step["lse_out"], workspace=ws)
+    torch.cuda.synchronize()
+    for what, res in (("two calls", two), ("step", step)):
+        assert_out(to64(res["o_part"]), o_ref, f"{what} o_part")
+        assert_lse(to64(res["lse_part"]), lp_ref, f"{what} lse_part", floor=True)
+        assert_out(to64(res["out"]), out_ref, f"{what} out")
+        assert_lse(to64(res["lse_out"]), lo_ref, f"{what} lse_out")
+        # the per-shard partials well inside the bar: 1e-5 relative to the row's scale
+        err = np.abs(to64(res["o_part"]) - o_ref).max(axis=-1)
+        assert (err <= 1e-5 * np.abs(o_ref).max(axis=-1) + 1e-6).all(), f"{what} o_part drift"
