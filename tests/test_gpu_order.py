@@ -66,7 +66,7 @@ def _check_oracle(w, inp, res, what):
         assert_lse(to64(res["lse_part"][:, b, hs]), ref["lse_part"], f"{what} lse_part b={b} h={h}",
                    floor=True)
         assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
-        assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}")
+        assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}", floor=True)
 
 
 def _check_entries(w, inp, ws):

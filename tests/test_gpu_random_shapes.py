@@ -15,10 +15,9 @@ import sys
 import numpy as np
 import pytest
 
-from oracle import oracle as orc
 from oracle import workloads as ow
 from synth import configs as sc
-from tests.helpers import assert_lse, assert_out, run_path, to64
+from tests.helpers import assert_lse, assert_out, assert_out_stored, run_path, to64
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -71,15 +70,14 @@ def _check(w, inp, res, opart, what):
             ref = ow.group(w, inp["lens_np"], b, h)
             hs = slice(h * w.G, (h + 1) * w.G)
             if opart == "fp32":
-                out_ref = ref["out"]
+                assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
             else:  # the exact partials rounded to the storage type, merged exactly
-                out_ref = np.stack([orc.merge_stored(ref["o_part"][:, g], ref["lse_part"][:, g], opart)[0]
-                                    for g in range(w.G)])
-            assert_out(to64(res["out"][b, hs]), out_ref, f"{what} out b={b} h={h}")
+                assert_out_stored(to64(res["out"][b, hs]), ref["o_part"], ref["lse_part"], opart,
+                                  f"{what} out b={b} h={h}")
             assert_out(to64(res["o_part"][:, b, hs]), ref["o_part"], f"{what} o_part b={b} h={h}")
             assert_lse(to64(res["lse_part"][:, b, hs]), ref["lse_part"], f"{what} lse_part b={b} h={h}",
                        floor=True)
-            assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}")
+            assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}", floor=True)
 
 
 @pytest.mark.parametrize("i", range(N_SHAPES), ids=_id)
