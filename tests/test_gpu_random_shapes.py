@@ -3,7 +3,8 @@
 Shapes are drawn from a fixed seed over shards, batch, heads (MHA to GQA 24,
 one or two head blocks), head dim, capacity, ragged or uniform lengths with
 empty shards, element type, partial storage type and an optional chunk
-length, so the planner lands on every form: one launch (whole shards, split
+length (a second, wider draw reaches 64 shards, GQA 32, one-token capacities
+and fp16 partials), so the planner lands on every form: one launch (whole shards, split
 shards, two levels), attention + row merge, attention + chunk combine +
 merge, and cpdec_attn_partial with and without its in-launch chunk combine.
 Each shape is checked against the oracle on every (sequence, kv head) group
@@ -25,6 +26,7 @@ import lse_merge_split_amd as cp  # noqa: E402
 from synth import gpu as sg  # noqa: E402
 
 N_SHAPES = 24
+N_WIDE = 60
 
 
 def _shapes():
@@ -46,7 +48,32 @@ def _shapes():
             ragged=ragged, L=0 if ragged else Lcap - int(rng.integers(0, 3)),
             empty_p=0.1 if ragged else 0.0, k_scale=float(rng.choice([1.0, 3.0])), seed=5000 + i)
         out.append((w, opart, chunk))
-    # forms the draw may miss: more than 64 chunks (chunk-combine launch in both
+    # a wider draw: up to 64 shards, GQA up to 32 (and odd group sizes), capacities
+    # from 1 token, fp16 partials, chunk lengths that are not powers of two
+    rng = np.random.default_rng(20261204)
+    wide = 0
+    while wide < N_WIDE:
+        R = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 13, 16, 33, 64]))
+        Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 17, 24, 32]))
+        D = int(rng.choice([64, 128, 256]))
+        B = int(rng.integers(1, 7))
+        Lcap = int(rng.choice([1, 5, 31, 32, 33, 64, 100, 257, 640, 1500, 3000, 5000]))
+        ragged = bool(rng.integers(0, 2))
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        opart = str(rng.choice(["fp32", "fp32", "bf16", "fp16"]))
+        chunk = int(rng.choice([0, 0, 32, 32, 64, 96, 256, 1024]))
+        L = max(0, Lcap - int(rng.integers(0, 3)))
+        k_scale = float(rng.choice([1.0, 3.0]))
+        if R * B * Hkv * G * D * Lcap > 60_000_000:   # keeps the oracle to seconds
+            continue
+        w = sc.WORKLOADS["c4"].scaled(
+            name=f"wide{wide}", R=R, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, Lcap=Lcap,
+            ragged=ragged, L=0 if ragged else L, empty_p=0.15 if ragged else 0.0,
+            k_scale=k_scale, seed=6000 + wide)
+        out.append((w, opart, chunk))
+        wide += 1
+    # forms the draws may miss: more than 64 chunks (chunk-combine launch in both
     # entry points), and the two-level one launch with 32- and 16-bit partials
     out.append((sc.small("c4", R=2, B=1, Hq=8, Hkv=2, Lcap=2500, seed=5100), "fp32", 32))
     out.append((sc.small("c4", B=2, Hq=32, Lcap=512, seed=5101), "fp32", 0))
