@@ -58,6 +58,8 @@
 //
 // Roofline: reading K and V once (2*D*2 bytes per token per kv head) is the
 // bound; the GQA group shares every K/V byte across its G heads.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -413,11 +415,21 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
       // (rare after the first tiles); the branch is wave-uniform and holds no loads
       const bool grew = __any(m_new > m);
       m = m_new;
+      // fp16 operands: the probabilities are taken relative to this tile's own
+      // max (its largest is then 1) and the tile's p.V is scaled by
+      // beta = 2^(tile max - running max) on its way into the accumulator.
+      // Relative to the running max, a tile far below an earlier dominant
+      // token would hold probabilities in fp16's subnormal range, where the
+      // hi + lo split keeps only an absolute step of 2^-24.  (bf16 has fp32's
+      // exponent range and takes the probabilities as they are, beta = 1.)
+      constexpr bool kTileRef = std::is_same<T, f16_t>::value;
+      const float p_ref = (kTileRef && mt != neg_inf()) ? mt : m_ref;
+      const float beta = kTileRef ? exp2f(p_ref - m_ref) : 1.f;
       float pr[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - m_ref);
+      for (int j = 0; j < 8; ++j) pr[j] = exp2f(x[j >> 2][j & 3] - p_ref);
       float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      lsum_d = __builtin_fma(lsum_d, (double)alpha, (double)ps);
+      lsum_d = __builtin_fma(lsum_d, (double)alpha, (double)ps * (double)beta);
 
       // A tile crossing the end: V rows past it (padding read by the first,
       // speculative load) become zeros, since 0 * NaN would poison the sums.
@@ -450,9 +462,14 @@ __device__ __forceinline__ bool attend_chunk(const Args& p, const void* kshard, 
           u32x4 va;
 #pragma unroll
           for (int k = 0; k < 4; ++k) va[k] = perm_b32(vr[nb][2 * k + 1][w], vr[nb][2 * k][w], sel);
-          f32x4 a = grew ? acc[nb][n] * alpha : acc[nb][n];
-          a = mfma16x16x32<T>(va, phi, a);
-          acc[nb][n] = mfma16x16x32<T>(va, plo, a);
+          const f32x4 a = grew ? acc[nb][n] * alpha : acc[nb][n];
+          if constexpr (kTileRef) {
+            f32x4 t = mfma16x16x32<T>(va, phi, f32x4{0.f, 0.f, 0.f, 0.f});
+            t = mfma16x16x32<T>(va, plo, t);
+            acc[nb][n] = a + t * beta;
+          } else {
+            acc[nb][n] = mfma16x16x32<T>(va, plo, mfma16x16x32<T>(va, phi, a));
+          }
         }
       }
   };

@@ -325,25 +325,26 @@ MAX_D = 128
 MAX_CAP = (2 ** 31 - 1) // (MAX_D * 2)          # 8,388,607 tokens
 
 
-def _max_cap_case():
-    a, bk = 12.0, 15.0                            # bf16-exact; a * bk / sqrt(128) = 15.91
+def _max_cap_case(dt="bf16"):
+    a, bk = 12.0, 15.0                            # exact in bf16 and fp16; a * bk / sqrt(128) = 15.91
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
     R, cap, D = 2, MAX_CAP, MAX_D
     lens = [cap, cap - 13]                        # full, and a ragged tail before NaN padding
     d = torch.arange(1, D + 1, dtype=torch.float64)
     vl = [d / 128, -d / 128]                      # per shard, bf16-exact
     vf = [-d / 256, -d / 512]
     c = [0.25, -0.125]
-    q = torch.zeros(1, 2, D, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 2, D, dtype=tdt, device="cuda")
     q[0, 0, 0], q[0, 1, 1] = a, a
     ks, vs = [], []
     for r in range(R):
         L = lens[r]
-        k = torch.zeros(1, 1, cap, D, dtype=torch.bfloat16, device="cuda")
-        v = torch.full((1, 1, cap, D), c[r], dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros(1, 1, cap, D, dtype=tdt, device="cuda")
+        v = torch.full((1, 1, cap, D), c[r], dtype=tdt, device="cuda")
         k[0, 0, 0, 1] = bk
         k[0, 0, L - 1, 0] = bk
-        v[0, 0, 0] = vf[r].to(torch.bfloat16).cuda()
-        v[0, 0, L - 1] = vl[r].to(torch.bfloat16).cuda()
+        v[0, 0, 0] = vf[r].to(tdt).cuda()
+        v[0, 0, L - 1] = vl[r].to(tdt).cuda()
         if L < cap:                               # padding past the length: NaN, never read
             k[0, 0, L:] = float("nan")
             v[0, 0, L:] = float("nan")
@@ -366,9 +367,10 @@ def _max_cap_case():
     return dict(q=q, k_shards=ks, v_shards=vs, lens=lens_t), o_ref, o_mag, lse_ref
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("chunk", [0, 2 ** 18, 2 ** 23],
                          ids=["library chunks", "longest chunks", "whole shard asked, 2^18 used"])
-def test_attn_max_capacity(chunk):
+def test_attn_max_capacity(chunk, dt):
     """Both attention entry points at the largest capacity.  Per-shard
     results against the magnitude of their terms: the FP32 p.V accumulation
     drifts by ~1e-7 of it per tile a wave adds on this input (~5e-5 at the
@@ -379,8 +381,8 @@ def test_attn_max_capacity(chunk):
     65536 tiles per wave of a whole shard the drift passes the output
     tolerance on this input."""
     from oracle import oracle as orc
-    _say(f"attn max capacity {MAX_CAP} tokens, chunk_tokens={chunk}: filling inputs")
-    inp, o_ref, o_mag, lse_ref = _max_cap_case()
+    _say(f"attn max capacity {MAX_CAP} tokens, {dt}, chunk_tokens={chunk}: filling inputs")
+    inp, o_ref, o_mag, lse_ref = _max_cap_case(dt)
     desc = cp.make_attn_desc(inp["q"], inp["k_shards"], chunk_tokens=chunk)
     plan = cp.attn_plan(desc)
     assert plan["chunk_tokens"] == (min(chunk, 2 ** 18) if chunk else 32768)
