@@ -13,8 +13,9 @@ from synth import configs as sc
 from .oracle import attend_shard, merge, NEG_INF
 
 
-def group(w: sc.Workload, lens: np.ndarray, b: int, h: int):
-    """Oracle for the G query heads of kv head h of sequence b, all shards.
+def group(w: sc.Workload, lens: np.ndarray, b: int, h: int, scale: float | None = None):
+    """Oracle for the G query heads of kv head h of sequence b, all shards,
+    with softmax scale ``scale`` (the workload's 1/sqrt(D) when None).
 
     Returns dict with o_part [R,G,D], lse_part [R,G], out [G,D], lse_out [G]
     (float64, unrounded)."""
@@ -26,7 +27,7 @@ def group(w: sc.Workload, lens: np.ndarray, b: int, h: int):
         L = int(lens[r, b])
         k = sc.kv_values(w, "k", r, b, h, L)
         v = sc.kv_values(w, "v", r, b, h, L)
-        o_part[r], lse_part[r] = attend_shard(qg, k, v, w.sm_scale)
+        o_part[r], lse_part[r] = attend_shard(qg, k, v, w.sm_scale if scale is None else scale)
     out = np.zeros((G, D))
     lse_out = np.full(G, NEG_INF)
     for g in range(G):

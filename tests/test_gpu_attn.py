@@ -460,3 +460,39 @@ def test_attn_attention_sink():
         # the per-shard partials well inside the bar: 1e-5 relative to the row's scale
         err = np.abs(to64(res["o_part"]) - o_ref).max(axis=-1)
         assert (err <= 1e-5 * np.abs(o_ref).max(axis=-1) + 1e-6).all(), f"{what} o_part drift"
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.3, 1.0])
+def test_attn_custom_scale(scale):
+    """An explicit softmax scale (sm_scale) in both entry points, against the
+    oracle with the same scale: a nearly flat softmax (0.02), a sharper one
+    (0.3) and a very peaky one (1.0 on k x3 scores, std ~30)."""
+    w = sc.small("c4", B=4, Hq=16, Hkv=4, Lcap=300)    # ragged, GQA 4, split shards
+    _say(f"attn custom scale {scale}")
+    inp = sg.attn_inputs(w)
+    q, R = inp["q"], w.R
+    o_part = torch.empty((R, w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((R, w.B, w.Hq), dtype=torch.float32, device="cuda")
+    cp.attn_partial(q, inp["k_shards"], inp["v_shards"], inp["lens"], o_part, lse_part, sm_scale=scale)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=q.dtype, device="cuda")
+    lse_out = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    cp.lse_merge(o_part, lse_part, out, lse_out)
+    step = dict(o_part=torch.empty_like(o_part), lse_part=torch.empty_like(lse_part),
+                out=torch.empty_like(out), lse_out=torch.empty_like(lse_out))
+    cp.cp_decode(q, inp["k_shards"], inp["v_shards"], inp["lens"], step["o_part"], step["lse_part"],
+                 step["out"], step["lse_out"], sm_scale=scale)
+    torch.cuda.synchronize()
+    two = dict(o_part=o_part, lse_part=lse_part, out=out, lse_out=lse_out)
+    for what, res in (("two calls", two), ("step", step)):
+        for (b, h) in all_groups(w):
+            ref = ow.group(w, inp["lens_np"], b, h, scale=scale)
+            hs = slice(h * w.G, (h + 1) * w.G)
+            assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
+            assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}",
+                       floor=True)
+            assert_out(to64(res["o_part"][:, b, hs]), ref["o_part"], f"{what} o_part b={b} h={h}")
+            assert_lse(to64(res["lse_part"][:, b, hs]), ref["lse_part"], f"{what} lse_part b={b} h={h}",
+                       floor=True)
+    # the default scale differs from these: the scale really reaches the kernel
+    ref0 = ow.group(w, inp["lens_np"], 0, 0)
+    assert not np.allclose(ref0["lse_out"], ow.group(w, inp["lens_np"], 0, 0, scale=scale)["lse_out"])
