@@ -186,6 +186,50 @@ def test_attn_strided_token_major_layout():
     res = run_path(inp2)
     for key in base:
         assert torch.equal(base[key], res[key]), key
+    # the whole step on the same strides
+    step = _step(inp2)
+    step_base = _step(inp)
+    for key in step_base:
+        assert torch.equal(step_base[key], step[key]), f"step {key}"
+
+
+def _step(inp, chunk=0):
+    q = inp["q"]
+    R, (B, Hq, D) = len(inp["k_shards"]), q.shape
+    res = dict(o_part=torch.empty((R, B, Hq, D), dtype=torch.float32, device="cuda"),
+               lse_part=torch.empty((R, B, Hq), dtype=torch.float32, device="cuda"),
+               out=torch.empty((B, Hq, D), dtype=q.dtype, device="cuda"),
+               lse_out=torch.empty((B, Hq), dtype=torch.float32, device="cuda"))
+    cp.cp_decode(q, inp["k_shards"], inp["v_shards"], inp["lens"], res["o_part"], res["lse_part"],
+                 res["out"], res["lse_out"], chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_attn_sliced_capacity_strides(chunk):
+    """K/V viewed out of a larger cache: each (sequence, kv head) row block
+    holds 37 more token rows than the capacity the call is given (head
+    stride (cap + 37) D), filled with NaN.  Both entry points give the same
+    bits as the contiguous layout, so nothing past the capacity is read."""
+    w = sc.small("c4", B=3, Hq=8, Hkv=2, Lcap=200)    # ragged, GQA 4
+    _say(f"attn sliced capacity strides, chunk {chunk}")
+    inp = sg.attn_inputs(w)
+    base, base_step = run_path(inp, chunk_tokens=chunk), _step(inp, chunk)
+    pad = 37
+    big_k = torch.full((w.R, w.B, w.Hkv, w.Lcap + pad, w.D), float("nan"), dtype=inp["k"].dtype,
+                       device="cuda")
+    big_v = torch.full_like(big_k, float("nan"))
+    big_k[:, :, :, :w.Lcap] = inp["k"]
+    big_v[:, :, :, :w.Lcap] = inp["v"]
+    inp2 = dict(inp)
+    inp2["k_shards"] = [big_k[r, :, :, :w.Lcap] for r in range(w.R)]
+    inp2["v_shards"] = [big_v[r, :, :, :w.Lcap] for r in range(w.R)]
+    assert inp2["k_shards"][0].stride(1) == (w.Lcap + pad) * w.D
+    res, res_step = run_path(inp2, chunk_tokens=chunk), _step(inp2, chunk)
+    for key in base:
+        assert torch.equal(base[key], res[key]), key
+        assert torch.equal(base_step[key], res_step[key]), f"step {key}"
 
 
 def test_attn_empty_shards_and_all_empty_sequence():
