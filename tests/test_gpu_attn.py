@@ -211,7 +211,8 @@ def test_attn_sliced_capacity_strides(chunk):
     """K/V viewed out of a larger cache: each (sequence, kv head) row block
     holds 37 more token rows than the capacity the call is given (head
     stride (cap + 37) D), filled with NaN.  Both entry points give the same
-    bits as the contiguous layout, so nothing past the capacity is read."""
+    bits as the contiguous layout, so nothing past the capacity is read; so
+    do shards that each live in an allocation of their own."""
     w = sc.small("c4", B=3, Hq=8, Hkv=2, Lcap=200)    # ragged, GQA 4
     _say(f"attn sliced capacity strides, chunk {chunk}")
     inp = sg.attn_inputs(w)
@@ -230,6 +231,14 @@ def test_attn_sliced_capacity_strides(chunk):
     for key in base:
         assert torch.equal(base[key], res[key]), key
         assert torch.equal(base_step[key], res_step[key]), f"step {key}"
+    # every shard in an allocation of its own (unrelated base addresses)
+    inp3 = dict(inp)
+    inp3["k_shards"] = [inp["k"][r].clone() for r in reversed(range(w.R))][::-1]
+    inp3["v_shards"] = [inp["v"][r].clone() for r in range(w.R)]
+    res3, res3_step = run_path(inp3, chunk_tokens=chunk), _step(inp3, chunk)
+    for key in base:
+        assert torch.equal(base[key], res3[key]), f"separate shards {key}"
+        assert torch.equal(base_step[key], res3_step[key]), f"separate shards step {key}"
 
 
 def test_attn_empty_shards_and_all_empty_sequence():
