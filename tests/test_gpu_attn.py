@@ -549,3 +549,38 @@ def test_attn_custom_scale(scale):
     # the default scale differs from these: the scale really reaches the kernel
     ref0 = ow.group(w, inp["lens_np"], 0, 0)
     assert not np.allclose(ref0["lse_out"], ow.group(w, inp["lens_np"], 0, 0, scale=scale)["lse_out"])
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_attn_shard_permutation(chunk):
+    """Permuting the shards (K/V pointers and lens rows together) permutes
+    the per-shard partials bit for bit (a shard's attention does not depend
+    on its index) and leaves the merged output within one output rounding
+    and the merged lse within 1e-6 (the merge sums in shard order), in both
+    entry points; the permuted run also meets the oracle."""
+    w = sc.small("c4", R=5, B=3, Hq=8, Hkv=2, Lcap=300)   # ragged with empty shards
+    _say(f"attn shard permutation, chunk {chunk}")
+    inp = sg.attn_inputs(w)
+    perm = [3, 0, 4, 2, 1]
+    inp_p = dict(inp)
+    inp_p["k_shards"] = [inp["k_shards"][r] for r in perm]
+    inp_p["v_shards"] = [inp["v_shards"][r] for r in perm]
+    inp_p["lens"] = inp["lens"][perm].contiguous()
+    inp_p["lens_np"] = inp["lens_np"][perm]
+    for what, run in (("two calls", lambda i: run_path(i, chunk_tokens=chunk)),
+                      ("step", lambda i: _step(i, chunk))):
+        base, res = run(inp), run(inp_p)
+        assert torch.equal(res["o_part"], base["o_part"][perm]), f"{what} o_part"
+        assert torch.equal(res["lse_part"], base["lse_part"][perm]), f"{what} lse_part"
+        assert torch.equal(torch.isneginf(res["lse_out"]), torch.isneginf(base["lse_out"]))
+        fin = torch.isfinite(base["lse_out"])
+        assert torch.allclose(res["lse_out"][fin], base["lse_out"][fin], rtol=1e-6, atol=1e-6)
+        d = (res["out"].float() - base["out"].float()).abs()
+        assert bool((d <= 2.0 ** -7 * base["out"].float().abs() + 1e-6).all()), f"{what} out"
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                ref = ow.group(w, inp["lens_np"], b, h)
+                hs = slice(h * w.G, (h + 1) * w.G)
+                assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
+                assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}",
+                           floor=True)
