@@ -228,8 +228,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the path has no cross-GPU step on one device).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path "
+              "here is one GPU's share of the work and has no cross-GPU step.", file=sys.stderr)
         sys.exit(2)
 
     import torch
