@@ -47,6 +47,7 @@ constexpr int kDefaultWaves = 4;        // waves per workgroup when shards are n
 constexpr int kSplitWaves = 2;          // waves per workgroup when shards are split
 constexpr int64_t kSplitBlocks = 512;   // fewer units than this: split shards into chunks,
                                         // aiming at this many workgroups
+constexpr int64_t kMinSplitBlocks = 256;  // one workgroup per CU at least
 // Longest chunk the library picks.  A wave accumulates its p.V sums in FP32
 // (MFMA accumulators), one rounding per tile; when one early token dominates
 // and the rest add nearly constant small terms, that rounding is biased, so
@@ -127,11 +128,32 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   // Split shards: the workgroup that merges a group in the one-launch step
   // needs a thread per (shard, head, float4) item; give it more waves when
   // that lets the group fit (a wave past the chunk's end simply sees no tile).
+  // When the library picked the chunks, it also makes them longer, so that
+  // the launch keeps about kSplitBlocks x kSplitWaves waves (one per SIMD) in
+  // at least kMinSplitBlocks workgroups: more waves over the same chunks left
+  // each wave 1-4 tiles and measured 9-50% slower (batch 1, MHA, 16 x 2048
+  // tokens at D = 64: 22.0 us with 4 waves over 256-token chunks, 14.7 us
+  // over 512-token chunks).
   if (!overrides().waves && p.nchunks > 1) {
     const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
     int w = p.waves;
     while (w < 8 && items > 64 * w) w *= 2;
-    if (items <= 64 * w) p.waves = w;
+    if (items <= 64 * w && w != p.waves) {
+      if (split) {
+        int64_t blocks = kSplitBlocks * p.waves / w;
+        if (blocks < kMinSplitBlocks) blocks = kMinSplitBlocks;
+        const int span_w = kTileTokens * w;
+        int64_t want = ceil_div(blocks, p.units);
+        const int64_t most = ceil_div(cap, span_w);
+        if (want > most) want = most;
+        int64_t c2 = ceil_div(ceil_div(cap, want), span_w) * span_w;
+        if (c2 > kMaxChunkTokens) c2 = kMaxChunkTokens;
+        if (ceil_div(cap, c2) > kMaxChunks) c2 = ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
+        p.chunk = (int)c2;
+        p.nchunks = (int)ceil_div(cap, c2);
+      }
+      p.waves = w;
+    }
   }
 
   const int64_t blocks = p.units * p.nchunks;
