@@ -48,6 +48,7 @@ constexpr int kSplitWaves = 2;          // waves per workgroup when shards are s
 constexpr int64_t kSplitBlocks = 512;   // fewer units than this: split shards into chunks,
                                         // aiming at this many workgroups
 constexpr int64_t kMinSplitBlocks = 256;  // one workgroup per CU at least
+constexpr int kMinWaveTiles = 8;          // tiles a wave should see in a split launch
 // Longest chunk the library picks.  A wave accumulates its p.V sums in FP32
 // (MFMA accumulators), one rounding per tile; when one early token dominates
 // and the rest add nearly constant small terms, that rounding is biased, so
@@ -128,32 +129,43 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   // Split shards: the workgroup that merges a group in the one-launch step
   // needs a thread per (shard, head, float4) item; give it more waves when
   // that lets the group fit (a wave past the chunk's end simply sees no tile).
-  // When the library picked the chunks, it also makes them longer, so that
-  // the launch keeps about kSplitBlocks x kSplitWaves waves (one per SIMD) in
-  // at least kMinSplitBlocks workgroups: more waves over the same chunks left
-  // each wave 1-4 tiles and measured 9-50% slower (batch 1, MHA, 16 x 2048
-  // tokens at D = 64: 22.0 us with 4 waves over 256-token chunks, 14.7 us
-  // over 512-token chunks).
+  // When the library picked the chunks, it also doubles their length while a
+  // wave would see fewer than kMinWaveTiles tiles and at least
+  // kMinSplitBlocks workgroups remain: more waves over the same short chunks
+  // measured 9-50% slower (batch 1, MHA, 16 x 2048 tokens at D = 64: 22.0 us
+  // with 4 waves over 256-token chunks, 14.7 us over 512-token chunks).
+  bool raised = false;
   if (!overrides().waves && p.nchunks > 1) {
     const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
     int w = p.waves;
     while (w < 8 && items > 64 * w) w *= 2;
     if (items <= 64 * w && w != p.waves) {
-      if (split) {
-        int64_t blocks = kSplitBlocks * p.waves / w;
-        if (blocks < kMinSplitBlocks) blocks = kMinSplitBlocks;
-        const int span_w = kTileTokens * w;
-        int64_t want = ceil_div(blocks, p.units);
-        const int64_t most = ceil_div(cap, span_w);
-        if (want > most) want = most;
-        int64_t c2 = ceil_div(ceil_div(cap, want), span_w) * span_w;
-        if (c2 > kMaxChunkTokens) c2 = kMaxChunkTokens;
-        if (ceil_div(cap, c2) > kMaxChunks) c2 = ceil_div(ceil_div(cap, kMaxChunks), kTileTokens) * kTileTokens;
-        p.chunk = (int)c2;
-        p.nchunks = (int)ceil_div(cap, c2);
-      }
       p.waves = w;
+      raised = true;
+      if (split) {
+        int64_t c = p.chunk;
+        while (c < (int64_t)kMinWaveTiles * kTileTokens * w && 2 * c <= kMaxChunkTokens &&
+               p.units * ceil_div(cap, 2 * c) >= kMinSplitBlocks)
+          c *= 2;
+        p.chunk = (int)c;
+        p.nchunks = (int)ceil_div(cap, c);
+      }
     }
+  }
+  // Split launches whose merger did not set the waves, with at least one full
+  // round of workgroups and long chunks: 2 or 4 waves, whichever fills the
+  // last round of resident workgroups better (these kernels hold one wave per
+  // SIMD, so kSplitBlocks x kSplitWaves / w workgroups at a time).  Batch 6,
+  // GQA 4, 8 x 8192 tokens (768 workgroups): 288 us with 2 waves (1.5
+  // rounds), 253 us with 4 (3 rounds).
+  if (split && !raised && !overrides().waves && p.nchunks > 1 &&
+      p.units * p.nchunks >= kSplitBlocks && p.chunk >= kMinWaveTiles * kTileTokens * 4) {
+    auto fill = [&](int w) {
+      const int64_t resident = kSplitBlocks * kSplitWaves / w;
+      const int64_t blocks = p.units * p.nchunks;
+      return (double)blocks / (double)(ceil_div(blocks, resident) * resident);
+    };
+    if (fill(4) > fill(p.waves) + 1e-9) p.waves = 4;
   }
 
   const int64_t blocks = p.units * p.nchunks;
