@@ -48,7 +48,8 @@ constexpr int kSplitWaves = 2;          // waves per workgroup when shards are s
 constexpr int64_t kSplitBlocks = 512;   // fewer units than this: split shards into chunks,
                                         // aiming at this many workgroups
 constexpr int64_t kMinSplitBlocks = 256;  // one workgroup per CU at least
-constexpr int kMinWaveTiles = 8;          // tiles a wave should see in a split launch
+constexpr int kMinWaveTiles = 8;          // tiles a wave should see after a wave raise
+constexpr int kSplitMinTiles = 4;         // tiles a wave should see in a split launch
 // Longest chunk the library picks.  A wave accumulates its p.V sums in FP32
 // (MFMA accumulators), one rounding per tile; when one early token dominates
 // and the rest add nearly constant small terms, that rounding is biased, so
@@ -119,7 +120,18 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
     int64_t want = split ? ceil_div(kSplitBlocks, p.units) : 1;
     const int64_t most = ceil_div(cap, span);      // chunks of one pass of all waves
     if (want > most) want = most;
+    // More than kStepTwoLevelMaxChunks chunks leave only the three-launch step
+    // (batch 1, 16 heads on one kv head, 8192 tokens at D = 256: 64.3 us with
+    // 128 chunks, 16.1 us with 64).
+    if (want > kStepTwoLevelMaxChunks) want = kStepTwoLevelMaxChunks;
     chunk = (int)(ceil_div(ceil_div(cap, want), span) * span);
+    // At least kSplitMinTiles tiles per wave while kMinSplitBlocks workgroups
+    // remain (8 shards x 4 heads x 2048 tokens at D = 64: 15.0 us over 128-token
+    // chunks, 11.6 us over 256).
+    if (split) {
+      const int64_t c_min = (int64_t)kSplitMinTiles * span;
+      if (chunk < c_min && p.units * ceil_div(cap, c_min) >= kMinSplitBlocks) chunk = (int)c_min;
+    }
   }
   if (chunk > kMaxChunkTokens) chunk = kMaxChunkTokens;  // a multiple of every span
   if (ceil_div(cap, chunk) > kMaxChunks)
@@ -134,19 +146,31 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   // kMinSplitBlocks workgroups remain: more waves over the same short chunks
   // measured 9-50% slower (batch 1, MHA, 16 x 2048 tokens at D = 64: 22.0 us
   // with 4 waves over 256-token chunks, 14.7 us over 512-token chunks).
+  // Where the waves as they are would merge through the row-merge launch, the
+  // raise needs each wave to keep at least 2 tiles of library-picked chunks
+  // (2 shards x 64 heads over 512 tokens: 14.5 us with 8 waves over a quarter
+  // tile each, 10.2 us with 2 waves and the row merge); where they would take
+  // the two-level merge, the one-level merge of the raise wins even over
+  // short chunks (16 shards x 2 heads over 1024 tokens at D = 64: 14.5 vs
+  // 17.9 us).  The raise stops at 4 waves for D = 256, whose 8-wave kernels
+  // spill registers to scratch (2.3-2.5x slower).
   bool raised = false;
   if (!overrides().waves && p.nchunks > 1) {
     const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
+    const int w_max = D >= 256 ? 4 : 8;
     int w = p.waves;
-    while (w < 8 && items > 64 * w) w *= 2;
+    while (w < w_max && items > 64 * w) w *= 2;
     if (items <= 64 * w && w != p.waves) {
-      p.waves = w;
-      raised = true;
+      int64_t c = p.chunk;
       if (split) {
-        int64_t c = p.chunk;
         while (c < (int64_t)kMinWaveTiles * kTileTokens * w && 2 * c <= kMaxChunkTokens &&
                p.units * ceil_div(cap, 2 * c) >= kMinSplitBlocks)
           c *= 2;
+      }
+      const bool two_level_as_is = (int64_t)p.Gb * (D / 4) <= 64LL * p.waves;
+      if (!split || two_level_as_is || c >= 2LL * kTileTokens * w) {
+        p.waves = w;
+        raised = true;
         p.chunk = (int)c;
         p.nchunks = (int)ceil_div(cap, c);
       }
@@ -162,10 +186,34 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
       p.units * p.nchunks >= kSplitBlocks && p.chunk >= kMinWaveTiles * kTileTokens * 4) {
     auto fill = [&](int w) {
       const int64_t resident = kSplitBlocks * kSplitWaves / w;
-      const int64_t blocks = p.units * p.nchunks;
-      return (double)blocks / (double)(ceil_div(blocks, resident) * resident);
+      const int64_t nblocks = p.units * p.nchunks;
+      return (double)nblocks / (double)(ceil_div(nblocks, resident) * resident);
     };
     if (fill(4) > fill(p.waves) + 1e-9) p.waves = 4;
+  }
+  // Split groups that no one-launch merge fits at the final waves (neither
+  // the shards' vectors nor one unit's vectors fit the workgroup's threads):
+  // the step takes the row merge when shards x chunks (rounded up to a power
+  // of two) fit one wave and its workgroup fits the shards' vectors, else a
+  // chunk-combine and a merge launch.  Library-picked chunks are made longer
+  // to fit the row merge where it can run (4 shards x 3 sequences x 16 heads
+  // over 4096 tokens at D = 256: 41.6 us with 32 chunks and three launches,
+  // 22.7 us with 16 and two).
+  if (split && p.nchunks > 1) {
+    const int64_t threads = 64LL * p.waves;
+    const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
+    const int R = d->num_shards;
+    int fit = 1;
+    while (fit * 2 * R <= 64) fit *= 2;            // chunks whose power of two fits with R
+    if (items > threads && (int64_t)p.Gb * (D / 4) > threads && fit >= 2 && p.nchunks > fit &&
+        row_merge_waves(R, fit, D, 0, 0) > 0) {
+      const int span_w = kTileTokens * p.waves;
+      const int64_t c = ceil_div(ceil_div(cap, fit), span_w) * span_w;
+      if (c <= kMaxChunkTokens) {
+        p.chunk = (int)c;
+        p.nchunks = (int)ceil_div(cap, c);
+      }
+    }
   }
 
   const int64_t blocks = p.units * p.nchunks;

@@ -44,14 +44,19 @@ CASES = {
     "fp16 GQA 2 split": (sc.small("c4", B=2, Hq=16, Lcap=256, dtype="fp16"), 0, 1),
     "GQA 32 D64, two head blocks, chunk 256 (two levels)":
         (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 256, 1),
-    "GQA 32 D64, two head blocks (attention, combine, merge)":
-        (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 0, 3),
+    "GQA 32 D64, two head blocks (attention + row merge)":
+        (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 0, 2),
+    "GQA 16 D256, 16 shards (attention, combine, merge)":
+        (sc.small("c3", R=16, B=1, Hq=32, Hkv=2, D=256, Lcap=1024, L=1000), 0, 3),
     "64 shards (the most), whole shards (attention + merge)":
         (sc.small("c3", R=64, B=2, Hq=4, Hkv=1, D=64, Lcap=96, L=90), 0, 2),
     "64 shards, ragged with empty shards (attention + merge)":
         (sc.small("c4", R=64, B=2, Hq=4, Hkv=1, D=64, Lcap=96), 0, 2),
     "1 shard, split": (sc.small("c3", R=1, B=3, Hq=8, Hkv=2, D=128, Lcap=700, L=650), 0, 1),
-    "1 shard, ragged, 47 chunks (two levels)": (sc.small("c4", R=1, B=1, Hq=8, Hkv=1, D=128, Lcap=3000), 0, 1),
+    "1 shard, ragged, 47 chunks of 64 (two levels)":
+        (sc.small("c4", R=1, B=1, Hq=8, Hkv=1, D=128, Lcap=3000), 64, 1),
+    "1 shard, ragged, 47 chunks (attention + row merge)":
+        (sc.small("c4", R=1, B=1, Hq=8, Hkv=1, D=128, Lcap=3000), 0, 2),
     "GQA 24, two head blocks (attention + row merge)":
         (sc.small("c3", R=4, B=2, Hq=48, Hkv=2, D=128, Lcap=1024, L=1000), 0, 2),
     "D64 G3": (sc.small("c3", R=5, B=3, Hq=6, Hkv=2, D=64, Lcap=97, L=97), 0, 1),
