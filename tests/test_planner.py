@@ -60,6 +60,10 @@ def test_plan_invariants(seed):
         assert waves in (1, 2, 4, 8)
         assert nch <= 256
         assert chunk <= 1 << 18  # short enough for the FP32 p.V accumulation
+        if d.head_dim == 256:
+            assert waves <= 4    # the 8-wave kernels at D = 256 spill registers
+        if not d.chunk_tokens:
+            assert nch <= 64     # more would leave only the three-launch step
         if d.chunk_tokens:  # as given, unless that makes more than 256 chunks
             if -(-cap // d.chunk_tokens) <= 256:
                 assert chunk == min(d.chunk_tokens, 1 << 18)
