@@ -199,19 +199,32 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   // to fit the row merge where it can run (4 shards x 3 sequences x 16 heads
   // over 4096 tokens at D = 256: 41.6 us with 32 chunks and three launches,
   // 22.7 us with 16 and two).
+  // Where that would cut the chunks by more than half, 4 waves that let the
+  // two-level merge fit are taken instead, over chunks of at least
+  // kSplitMinTiles tiles per wave while kMinSplitBlocks workgroups remain (16
+  // shards x 8 heads over 8192 tokens: 43.4 us over 4 chunks and the row
+  // merge, 28.8 us with 4 waves over 16 chunks in one launch).
   if (split && p.nchunks > 1) {
     const int64_t threads = 64LL * p.waves;
     const int64_t items = (int64_t)d->num_shards * p.Gb * (D / 4);
     const int R = d->num_shards;
     int fit = 1;
     while (fit * 2 * R <= 64) fit *= 2;            // chunks whose power of two fits with R
-    if (items > threads && (int64_t)p.Gb * (D / 4) > threads && fit >= 2 && p.nchunks > fit &&
-        row_merge_waves(R, fit, D, 0, 0) > 0) {
+    if (items > threads && (int64_t)p.Gb * (D / 4) > threads && fit >= 2 && p.nchunks > fit) {
       const int span_w = kTileTokens * p.waves;
       const int64_t c = ceil_div(ceil_div(cap, fit), span_w) * span_w;
-      if (c <= kMaxChunkTokens) {
+      if (p.nchunks <= 2 * fit && row_merge_waves(R, fit, D, 0, 0) > 0 && c <= kMaxChunkTokens) {
         p.chunk = (int)c;
         p.nchunks = (int)ceil_div(cap, c);
+      } else if (!overrides().waves && p.waves < 4 && (int64_t)p.Gb * (D / 4) <= 64 * 4 &&
+                 p.nchunks <= kStepTwoLevelMaxChunks) {
+        p.waves = 4;
+        const int64_t c_min = (int64_t)kSplitMinTiles * kTileTokens * 4;
+        if (p.chunk < c_min && c_min <= kMaxChunkTokens &&
+            p.units * ceil_div(cap, c_min) >= kMinSplitBlocks) {
+          p.chunk = (int)c_min;
+          p.nchunks = (int)ceil_div(cap, c_min);
+        }
       }
     }
   }
