@@ -109,9 +109,13 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
   // Shards are split into chunks only when the units alone cannot fill the
   // GPU (every chunk costs a partial write and a merge).  Split problems are
   // latency-bound: fewer, smaller workgroups with two tiles per wave in
-  // flight measured fastest (c2: 23 vs 27 us).
+  // flight measured fastest (c2: 23 vs 27 us).  Exactly kMinSplitBlocks units
+  // (one workgroup per CU) stay whole: over two samples of random shapes
+  // (100 in all) that put 6 more within 8% of the best plan measured and
+  // none more than 5% slower (4 shards x 8 sequences x 8 kv heads over 512
+  // tokens: 18.6 vs 23.2 us).
   const bool split = d->chunk_tokens == 0 && overrides().chunk == 0 && p.units < kSplitBlocks &&
-                     cap > (int64_t)kTileTokens * kDefaultWaves;
+                     p.units != kMinSplitBlocks && cap > (int64_t)kTileTokens * kDefaultWaves;
   p.waves = overrides().waves ? overrides().waves : (split ? kSplitWaves : kDefaultWaves);
   const int span = kTileTokens * p.waves;  // tokens one pass of all waves covers
 

@@ -39,8 +39,8 @@ CASES = {
     "D256 G20 (over the merging workgroup: attention + row merge)":
         (sc.small("c3", R=3, B=2, Hq=40, Hkv=2, D=256, Lcap=300, L=290), 0, 2),
     "ragged GQA 8, B2 split, 8 x 32 chunks (4 waves: two levels)": (sc.small("c4", B=2, Lcap=1024), 32, 1),
-    "fp16 GQA 8 split (attention + row merge)": (sc.small("c4", B=4, Lcap=256, dtype="fp16"), 0, 2),
-    "fp16 GQA 4 split (two levels)": (sc.small("c4", B=4, Hq=32, Lcap=256, dtype="fp16"), 0, 1),
+    "fp16 GQA 8 split (attention + row merge)": (sc.small("c4", B=3, Lcap=256, dtype="fp16"), 0, 2),
+    "fp16 GQA 4 split (two levels)": (sc.small("c4", B=3, Hq=32, Lcap=256, dtype="fp16"), 0, 1),
     "fp16 GQA 2 split": (sc.small("c4", B=2, Hq=16, Lcap=256, dtype="fp16"), 0, 1),
     "GQA 32 D64, two head blocks, chunk 256 (two levels)":
         (sc.small("c3", R=8, B=1, Hq=64, Hkv=2, D=64, Lcap=2048, L=1900), 256, 1),
