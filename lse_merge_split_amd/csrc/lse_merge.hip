@@ -105,9 +105,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   const rsrc_t lrs = make_rsrc(lse, (uint32_t)((int64_t)R * rows * sizeof(float)));
   const uint32_t roff = (uint32_t)(row * D * sizeof(Tin)) + (uint32_t)(li * 16);
 
-  // Row max over shards: lane li reads shards li, li+GS, ..., then the group reduces.
-  float M = neg_inf();
-  for (int r = li; r < R; r += GS) M = fmaxf(M, buf4f(lrs, (uint32_t)(((int64_t)r * rows + row) * 4)));
+  // Row max over shards: lane li reads shards li, li+GS, ..., then the group
+  // reduces.  The first block's value is kept for the weights (one load).
+  const float l_first = (li < R) ? buf4f(lrs, (uint32_t)(((int64_t)li * rows + row) * 4)) : neg_inf();
+  float M = l_first;
+  for (int r = li + GS; r < R; r += GS) M = fmaxf(M, buf4f(lrs, (uint32_t)(((int64_t)r * rows + row) * 4)));
 #pragma unroll
   for (int off = GS / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, GS));
 
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   for (int rb = 0; rb < R; rb += GS) {
     // lane li owns shard rb + li of this block (its lse is cached from above)
     const int rl = rb + li;
-    const float lme = (rl < R) ? buf4f(lrs, (uint32_t)(((int64_t)rl * rows + row) * 4)) : neg_inf();
+    const float lme = rb == 0 ? l_first
+                              : (rl < R) ? buf4f(lrs, (uint32_t)(((int64_t)rl * rows + row) * 4)) : neg_inf();
     const int nb = min(GS, R - rb);
     for (int j0 = 0; j0 < nb; j0 += kBatch) {
       float lj[kBatch];
