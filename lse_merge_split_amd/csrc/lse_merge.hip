@@ -84,8 +84,10 @@ constexpr int kBatch = 8;  // shards whose loads are in flight together
 // fit on a CU).  Lane li of a row group owns shards li, li + GS, ...: it
 // loads their lse, the group takes the max, then every live shard's row is
 // requested before the FP64 exps are computed, so the arithmetic overlaps the
-// loads.  Batches of kBatch shards keep 8 x 16 bytes per lane in flight.
-template <typename Tin, typename Tout, int D>
+// loads.  Batches of KB shards keep KB x 16 bytes per lane in flight: KB = 8,
+// or 2 for R <= 2, whose smaller register set lets more waves share a SIMD
+// (they are what hides the latency when each wave carries little data).
+template <typename Tin, typename Tout, int D, int KB>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
     const Tin* __restrict__ o, const float* __restrict__ lse, int R, int64_t rows,
     Tout* __restrict__ out, float* __restrict__ lse_out) {
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
   constexpr int GS = NV < 64 ? NV : 64;    // lanes per row
   constexpr int RPW = 64 / GS;             // rows per wave
   constexpr int VPL = NV / GS;             // vectors per lane
-  static_assert(NV % GS == 0 && 64 % GS == 0 && GS >= kBatch, "row split");
+  static_assert(NV % GS == 0 && 64 % GS == 0 && GS >= KB, "row split");
 
   const int lane = threadIdx.x & 63;
   const int64_t row_raw = ((int64_t)blockIdx.x * kMergeWaves + wave_id()) * RPW + lane / GS;
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
     const float lme = rb == 0 ? l_first
                               : (rl < R) ? buf4f(lrs, (uint32_t)(((int64_t)rl * rows + row) * 4)) : neg_inf();
     const int nb = min(GS, R - rb);
-    for (int j0 = 0; j0 < nb; j0 += kBatch) {
-      float lj[kBatch];
-      u32x4 raw[kBatch][VPL];
+    for (int j0 = 0; j0 < nb; j0 += KB) {
+      float lj[KB];
+      u32x4 raw[KB][VPL];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
+      for (int j = 0; j < KB; ++j) {
         const float l = __shfl(lme, base + min(j0 + j, nb - 1));
         lj[j] = (j0 + j < nb) ? l : neg_inf();
         // an empty shard's row is never read: its offset is out of range (zeros)
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(
       // the exps of this batch's shards, computed while the rows load
       const double e_own = (lme != neg_inf()) ? exp((double)lme - Md) : 0.0;
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
+      for (int j = 0; j < KB; ++j) {
         const double ej = __shfl(e_own, base + min(j0 + j, nb - 1));
         if (lj[j] == neg_inf() || ej == 0.0) continue;  // never read, never used
         S += ej;
@@ -282,9 +284,18 @@ hipError_t launch_typed(const void* o, const float* lse, int R, int64_t rows, vo
   constexpr int GS = NV < 64 ? NV : 64;
   constexpr int rows_per_block = kMergeWaves * (64 / GS);
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D>), dim3((unsigned)blocks),
-                     dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
-                     static_cast<Tout*>(out), lse_out);
+  if (R <= 2)
+    hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D, 2>), dim3((unsigned)blocks),
+                       dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
+                       static_cast<Tout*>(out), lse_out);
+  else if (R <= 4)
+    hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D, 4>), dim3((unsigned)blocks),
+                       dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
+                       static_cast<Tout*>(out), lse_out);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<Tin, Tout, D, kBatch>), dim3((unsigned)blocks),
+                       dim3(kMergeWaves * 64), 0, s, static_cast<const Tin*>(o), lse, R, rows,
+                       static_cast<Tout*>(out), lse_out);
   return hipGetLastError();
 }
 
