@@ -25,8 +25,10 @@
 //     without touching memory, so their bytes are never read and garbage/NaN
 //     in them cannot leak.
 //   * Partial rows are read through buffer loads with the non-temporal
-//     (streaming) policy; batches of 8 shards keep 8 x 16 bytes per lane in
-//     flight.
+//     (streaming) policy, in batches of shards whose 16-byte loads are in
+//     flight together (8 shards per batch for a row per wave or R > 32; 2 or
+//     4 for rows of several per wave, where a smaller register set lets more
+//     waves share a SIMD).
 #include "device_common.h"
 #include "kernels.h"
 
