@@ -70,11 +70,26 @@ def test_merge_head_dims(D, in_dt):
     assert_lse(to64(lo), ref_lse)
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 8, 9, 13, 64])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 9, 13, 32, 33, 64])
 def test_merge_shard_counts(R):
+    """Shard counts on both sides of each load-batch size (2 shards per batch
+    up to R = 2, 4 up to R = 32, else 8)."""
     _say(f"merge R={R}")
     o_host, lse = make_case(R, 70, 128, "bf16", seed=100 + R, empty_p=0.2, sigma=16.0)
     out, lo = run_merge(o_host, lse, "bf16")
+    ref, ref_lse = oracle.merge_rows(o_host.double().numpy(), lse)
+    assert_out(to64(out), ref)
+    assert_lse(to64(lo), ref_lse)
+
+
+@pytest.mark.parametrize("R", [2, 4, 33])
+@pytest.mark.parametrize("D,in_dt", [(64, "fp32"), (64, "bf16"), (256, "fp32")])
+def test_merge_batch_sizes_across_row_widths(R, D, in_dt):
+    """Each load-batch size with rows of 128 B to 1 KB (4 to 16 rows or 1 row
+    per wave), 20% empty shards, ragged row count."""
+    _say(f"merge R={R} D={D} {in_dt}")
+    o_host, lse = make_case(R, 301, D, in_dt, seed=500 + R + D, empty_p=0.2, sigma=8.0)
+    out, lo = run_merge(o_host, lse, "fp16")
     ref, ref_lse = oracle.merge_rows(o_host.double().numpy(), lse)
     assert_out(to64(out), ref)
     assert_lse(to64(lo), ref_lse)
