@@ -171,22 +171,44 @@ _WS_CACHE: dict = {}
 
 
 def _workspace(device, nbytes, stream=None):
-    """A workspace of at least nbytes, reused across calls and shapes on the
-    current stream of `device` (one per stream: calls on different streams
-    may overlap and must not share one).  It is zero-filled when allocated:
-    both attention entry points need its counter region to start at zero,
-    and every completed call leaves it zero.  Calls marshalled once
-    (AttnCall, StepCall) keep the workspace of the stream current when they
-    were made."""
+    """A workspace of at least nbytes for the stream `stream` (a hipStream_t
+    handle; None: the current stream of `device`), reused across calls and
+    shapes on that stream.  Calls on different streams may overlap, so each
+    stream has its own.  Both attention entry points need the counter region
+    to start at zero and leave it zero, so a new workspace is zero-filled --
+    on `stream` itself, which also makes it that stream's allocation for
+    torch's caching allocator: the fill is ordered before the kernels that
+    use it, and a workspace replaced by a larger one is only handed out again
+    after the work already enqueued on that stream."""
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream(device).cuda_stream
-    key = (str(device), stream)
+    key = (str(device), int(stream))
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        current = torch.cuda.current_stream(device)
+        target = current if current.cuda_stream == stream else \
+            torch.cuda.ExternalStream(stream, device=device)
+        with torch.cuda.stream(target):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS_CACHE[key] = ws
     return ws
+
+
+def _check_tensors(named, device=None):
+    """Every tensor a GPU tensor on one device (a host pointer handed to a
+    kernel would fault the GPU).  `named` maps names to tensors (None
+    skipped).  Returns the device."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, other tensors on {device}")
+    return device
 
 
 class AttnCall:
@@ -194,26 +216,43 @@ class AttnCall:
 
     Calling it enqueues the kernel(s) on the current stream (or ``stream``).
     A workspace passed in must have its first STEP_COUNTER_BYTES bytes zero
-    before the first call (see workspace_clear); without one, the binding
-    picks its zero-filled workspace of the stream given as ``stream`` here
-    (default: the current stream), so calls made for different streams never
-    share one."""
+    before the first call (see workspace_clear) and belongs to the caller:
+    calls that may overlap need separate ones.  Without one, the binding uses
+    its zero-filled workspace of the stream the call is enqueued on, so calls
+    on different streams never share one.
+
+    Every argument is checked before anything reaches the library: each
+    tensor must be a GPU tensor on q's device, K and V must have q's dtype,
+    lens must be int32 and lse_part float32."""
 
     _workspace_query = staticmethod(attn_workspace_bytes)
+    _entry = "cpdec_attn_partial"
 
     def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, *, sm_scale=0.0,
                  kv_capacity=None, workspace=None, chunk_tokens=0, stream=None):
         torch = _torch()
-        if len(k_shards) != len(v_shards):
-            raise ValueError("k_shards and v_shards differ in length")
+        k_shards, v_shards = list(k_shards), list(v_shards)
+        if not k_shards or len(k_shards) != len(v_shards):
+            raise ValueError("k_shards and v_shards must be non-empty and of one length")
         for v, k in zip(v_shards, k_shards):
             if v.shape != k.shape or v.stride() != k.stride():
                 raise ValueError("V shards must match K shards in shape and strides")
+        if q.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"q must be float16 or bfloat16, not {q.dtype}")
+        for name, t in (("k_shards", k_shards), ("v_shards", v_shards)):
+            if any(x.dtype != q.dtype for x in t):
+                raise TypeError(f"every tensor of {name} must have q's dtype {q.dtype}")
         if not (q.is_contiguous() and o_part.is_contiguous() and lse_part.is_contiguous()
                 and lens.is_contiguous()):
             raise ValueError("q, o_part, lse_part and lens must be contiguous")
         if lens.dtype != torch.int32 or lse_part.dtype != torch.float32:
             raise TypeError("lens must be int32 and lse_part float32")
+        if workspace is not None and not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        tensors = {"q": q, "lens": lens, "o_part": o_part, "lse_part": lse_part,
+                   "workspace": workspace}
+        tensors.update({f"k_shards[{r}]": k for r, k in enumerate(k_shards)})
+        tensors.update({f"v_shards[{r}]": v for r, v in enumerate(v_shards)})
         desc = make_attn_desc(q, k_shards, kv_capacity=kv_capacity, sm_scale=sm_scale,
                               opart_dtype=o_part.dtype, chunk_tokens=chunk_tokens)
         R = len(k_shards)
@@ -222,58 +261,87 @@ class AttnCall:
         if (tuple(lse_part.shape) != (R, desc.batch, desc.num_q_heads)
                 or tuple(lens.shape) != (R, desc.batch)):
             raise ValueError("lse_part must be [R, B, Hq] and lens [R, B]")
+        self._tensors = tensors
+        self._setup(desc, workspace)
+        if stream is not None:
+            self._args_for(_stream_handle(stream))   # the stream's workspace, allocated now
+
+    def _setup(self, desc, workspace):
+        """Check devices, plan, and marshal the pointers (StepCall adds its
+        own tensors and outputs)."""
+        t = self._tensors
+        self._device = _check_tensors(t)
+        R = desc.num_shards
+        self.desc = desc
         self.workspace_bytes = self._workspace_query(desc)
         self.plan = attn_plan(desc)
-        if workspace is None and self.workspace_bytes > 0:
-            workspace = _workspace(q.device, self.workspace_bytes, _stream_handle(stream))
-        self._keep = (q, list(k_shards), list(v_shards), lens, o_part, lse_part, workspace)
-        self.desc = desc
-        self._device = q.device
-        ks = (ctypes.c_void_p * R)(*[k.data_ptr() for k in k_shards])
-        vs = (ctypes.c_void_p * R)(*[v.data_ptr() for v in v_shards])
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        self._args = [ctypes.byref(desc), q.data_ptr(), ks, vs, lens.data_ptr(), o_part.data_ptr(),
-                      lse_part.data_ptr(), ws_ptr, ws_bytes]
+        self._own_ws = workspace
+        ks = (ctypes.c_void_p * R)(*[t[f"k_shards[{r}]"].data_ptr() for r in range(R)])
+        vs = (ctypes.c_void_p * R)(*[t[f"v_shards[{r}]"].data_ptr() for r in range(R)])
         self._arrays = (ks, vs)
-        self._fn = lib().cpdec_attn_partial
+        self._head = [ctypes.byref(desc), t["q"].data_ptr(), ks, vs, t["lens"].data_ptr()]
+        self._outs = [t["o_part"].data_ptr(), t["lse_part"].data_ptr()]
+        self._fn = getattr(lib(), self._entry)
+        self._by_stream = {}
+
+    def _args_for(self, stream: int):
+        args = self._by_stream.get(stream)
+        if args is None:
+            ws = self._own_ws
+            if ws is None and self.workspace_bytes > 0:
+                ws = _workspace(self._device, self.workspace_bytes, stream)
+            ws_ptr = ws.data_ptr() if ws is not None else None
+            ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+            args = (self._head + self._outs + [ws_ptr, ws_bytes], ws)
+            self._by_stream[stream] = args
+        return args
+
+    def workspace(self, stream=None):
+        """The workspace a call on `stream` uses (None when it needs none)."""
+        stream = _stream_handle(stream)
+        if stream is None:
+            stream = _torch().cuda.current_stream(self._device).cuda_stream
+        return self._args_for(stream)[1]
 
     def __call__(self, stream=None):
         """Enqueue on `stream` (a hipStream_t handle), else torch's current stream."""
+        stream = _stream_handle(stream)
         if stream is None:
             stream = _torch().cuda.current_stream(self._device).cuda_stream
-        rc = self._fn(*self._args, stream)
+        rc = self._fn(*self._args_for(stream)[0], stream)
         if rc != 0:
-            raise CpdecError(rc, "cpdec_attn_partial")
+            raise CpdecError(rc, self._entry)
 
 
 class StepCall(AttnCall):
     """A cpdec_cp_decode call (the whole step: partials and their merge,
     normally one launch) with its arguments marshalled once.  A workspace
     passed in must have its first STEP_COUNTER_BYTES bytes zero before the
-    first call (see workspace_clear)."""
+    first call (see workspace_clear).  out must be [B, Hq, D] of q's dtype
+    and lse_out (optional) [B, Hq] float32, on q's device."""
 
     _workspace_query = staticmethod(step_workspace_bytes)
+    _entry = "cpdec_cp_decode"
 
     def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, **kw):
-        super().__init__(q, k_shards, v_shards, lens, o_part, lse_part, **kw)
-        self.launches = step_launches(self.desc)
+        torch = _torch()
         if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
             raise ValueError("out must be a contiguous [B, Hq, D] tensor of q's dtype")
-        if lse_out is not None and (tuple(lse_out.shape) != tuple(q.shape[:2])
-                                    or not lse_out.is_contiguous()):
-            raise ValueError("lse_out must be a contiguous [B, Hq] float32 tensor")
-        self._keep = self._keep + (out, lse_out)
-        a = self._args
-        self._args = a[:7] + [out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None] + a[7:]
-        self._fn = lib().cpdec_cp_decode
+        if lse_out is not None:
+            if lse_out.dtype != torch.float32:
+                raise TypeError(f"lse_out must be float32, not {lse_out.dtype}")
+            if tuple(lse_out.shape) != tuple(q.shape[:2]) or not lse_out.is_contiguous():
+                raise ValueError("lse_out must be a contiguous [B, Hq] float32 tensor")
+        self._step_outs = (out, lse_out)
+        super().__init__(q, k_shards, v_shards, lens, o_part, lse_part, **kw)
 
-    def __call__(self, stream=None):
-        if stream is None:
-            stream = _torch().cuda.current_stream(self._device).cuda_stream
-        rc = self._fn(*self._args, stream)
-        if rc != 0:
-            raise CpdecError(rc, "cpdec_cp_decode")
+    def _setup(self, desc, workspace):
+        out, lse_out = self._step_outs
+        self._tensors.update({"out": out, "lse_out": lse_out})
+        super()._setup(desc, workspace)
+        self._outs = self._outs + [out.data_ptr(),
+                                   lse_out.data_ptr() if lse_out is not None else None]
+        self.launches = step_launches(desc)
 
 
 def cp_decode(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, *, stream=None,
@@ -285,28 +353,39 @@ def cp_decode(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, 
 
 class MergeCall:
     """A cpdec_lse_merge call with its arguments marshalled once:
-    o_part [R, ..., D] and lse_part [R, ...] into out [..., D], lse_out [...]."""
+    o_part [R, ..., D] and lse_part [R, ...] into out [..., D], lse_out [...].
+    lse_part and lse_out must be float32; every tensor a GPU tensor on one
+    device."""
 
     def __init__(self, o_part, lse_part, out, lse_out=None):
+        torch = _torch()
+        if o_part.dim() < 2:
+            raise ValueError("o_part must be [R, ..., D]")
         R = o_part.shape[0]
         D = o_part.shape[-1]
-        rows = o_part.numel() // (R * D)
+        rows = o_part.numel() // (R * D) if R * D else 0
         if not (o_part.is_contiguous() and lse_part.is_contiguous() and out.is_contiguous()):
             raise ValueError("o_part, lse_part and out must be contiguous")
+        if lse_part.dtype != torch.float32:
+            raise TypeError(f"lse_part must be float32, not {lse_part.dtype}")
+        if lse_out is not None and lse_out.dtype != torch.float32:
+            raise TypeError(f"lse_out must be float32, not {lse_out.dtype}")
+        in_code, out_code = dtype_code(o_part.dtype), dtype_code(out.dtype)
         if lse_part.numel() != R * rows or out.numel() != rows * D:
             raise ValueError("shape mismatch between o_part, lse_part and out")
         if lse_out is not None and (lse_out.numel() != rows or not lse_out.is_contiguous()):
             raise ValueError("lse_out must hold one value per row")
+        self._device = _check_tensors({"o_part": o_part, "lse_part": lse_part, "out": out,
+                                       "lse_out": lse_out})
         self._keep = (o_part, lse_part, out, lse_out)
-        self._device = o_part.device
         self.rows, self.R, self.D = rows, R, D
-        self._args = [o_part.data_ptr(), lse_part.data_ptr(), R, rows, D, dtype_code(o_part.dtype),
-                      dtype_code(out.dtype), out.data_ptr(),
-                      lse_out.data_ptr() if lse_out is not None else None]
+        self._args = [o_part.data_ptr(), lse_part.data_ptr(), R, rows, D, in_code, out_code,
+                      out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None]
         self._fn = lib().cpdec_lse_merge
 
     def __call__(self, stream=None):
         """Enqueue on `stream` (a hipStream_t handle), else torch's current stream."""
+        stream = _stream_handle(stream)
         if stream is None:
             stream = _torch().cuda.current_stream(self._device).cuda_stream
         rc = self._fn(*self._args, stream)
@@ -330,13 +409,17 @@ def lse_merge(o_part, lse_part, out, lse_out=None, *, stream=None):
 
 
 def _stream_handle(stream):
+    """A hipStream_t handle as an int from a handle or a torch stream (None stays None)."""
     if stream is None:
         return None
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def workspace_clear(ws, *, stream=None):
+    """Zero-fill a workspace tensor with the library's clear kernel on `stream`
+    (default: the current stream); needed once for a new workspace."""
     torch = _torch()
+    _check_tensors({"workspace": ws})
     s = _stream_handle(stream)
     if s is None:
         s = torch.cuda.current_stream(ws.device).cuda_stream

@@ -34,7 +34,9 @@ Pins: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` against closed forms, hand-derived values,
 brute force, an independent library routine and the method's invariants;
 ``tests/test_oracle_mutations.py`` plants plausible mistakes in copies of
-these functions and checks that the pins catch each one.
+these functions and checks that the pins catch each one.  The workload glue
+in ``oracle/workloads.py`` is tied to ``cp_decode`` and ``merge_rows`` over
+whole materialised workloads by ``tests/test_oracle_workloads.py``.
 """
 from __future__ import annotations
 
@@ -163,28 +165,3 @@ def cp_decode(q: np.ndarray, k_shards, v_shards, lens: np.ndarray, Hkv: int,
         for hq in range(Hq):
             out[b, hq], lse_out[b, hq] = merge(o_part[:, b, hq], lse_part[:, b, hq])
     return o_part, lse_part, out, lse_out
-
-
-def attend_unsplit(q: np.ndarray, k_shards, v_shards, lens: np.ndarray, Hkv: int,
-                   scale: float | None = None):
-    """Attention over the concatenation of every shard's valid tokens.
-
-    This is what the merge must reproduce ([CP] "Introduction": splitting the
-    KV sequence and merging the partials gives ordinary attention).
-    Returns (out [B,Hq,D], lse [B,Hq])."""
-    q = np.asarray(q, dtype=np.float64)
-    B, Hq, D = q.shape
-    G = Hq // Hkv
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    out = np.zeros((B, Hq, D))
-    lse = np.full((B, Hq), NEG_INF)
-    for b in range(B):
-        for h in range(Hkv):
-            k = np.concatenate([np.asarray(ks[b, h, :int(lens[r][b])], dtype=np.float64)
-                                for r, ks in enumerate(k_shards)], axis=0)
-            v = np.concatenate([np.asarray(vs[b, h, :int(lens[r][b])], dtype=np.float64)
-                                for r, vs in enumerate(v_shards)], axis=0)
-            heads = slice(h * G, (h + 1) * G)
-            out[b, heads], lse[b, heads] = attend_shard(q[b, heads], k, v, scale)
-    return out, lse

@@ -299,6 +299,21 @@ def test_attn_split_invariance_on_gpu():
 
 
 # ------------------------------------------------------------------ full sizes
+def _compare_full(w, res, refs, what):
+    """Sampled groups of a full-size run against the oracle: every output
+    element, the merged lse at the strict 1e-5 relative bar (at these sizes
+    |lse| is far from 0, so the max(1, |lse|) floor is not needed), the
+    per-shard partials as diagnostics."""
+    G = w.G
+    for (b, h), ref in refs.items():
+        hs = slice(h * G, (h + 1) * G)
+        assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
+        assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}")
+        assert_out(to64(res["o_part"][:, b, hs]), ref["o_part"], f"{what} o_part b={b} h={h}")
+        assert_lse(to64(res["lse_part"][:, b, hs]), ref["lse_part"], f"{what} lse_part b={b} h={h}",
+                   floor=True)
+
+
 def _full(name, groups_fn):
     w = sc.WORKLOADS[name]
     _say(f"attn full {name}: allocating and filling inputs")
@@ -319,9 +334,7 @@ def _full(name, groups_fn):
     nl = live.sum(axis=0)
     assert np.all(lse_out[anylive] >= Mx[anylive] - 1e-5 * np.abs(Mx[anylive]))
     assert np.all(lse_out[anylive] <= Mx[anylive] + np.log(nl[anylive]) + 1e-5 * np.abs(Mx[anylive]))
-    _say(f"attn full {name}: oracle on sampled groups")
-    check_groups(w, inp, res, groups_fn(w, lens))
-    # the whole step (one launch) on the same inputs
+    # the whole step on the same inputs, in the launch configuration the benchmark times
     _say(f"attn full {name}: whole step")
     step = {k: torch.empty_like(v) for k, v in res.items()}
     desc = cp.make_attn_desc(inp["q"], inp["k_shards"])
@@ -339,9 +352,21 @@ def _full(name, groups_fn):
     # against the two calls: one output rounding apart at most
     d = (step["out"].float() - res["out"].float()).abs()
     assert bool((d <= 2.0 ** -7 * res["out"].float().abs() + 1e-6).all())
-    check_groups(w, inp, step, groups_fn(w, lens))
-    del inp, res, step
+    res = {k: v.cpu() for k, v in res.items()}
+    step = {k: v.cpu() for k, v in step.items()}
+    del inp, ws
     torch.cuda.empty_cache()
+    groups = groups_fn(w, lens)
+    _say(f"attn full {name}: oracle on {len(groups)} sampled groups")
+    refs = {(b, h): ow.group(w, lens, b, h) for (b, h) in groups}
+    _compare_full(w, res, refs, "two calls")
+    _compare_full(w, step, refs, "step")
+
+
+def _random_groups(w, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(w.B * w.Hkv, size=n, replace=False)
+    return [(int(i) // w.Hkv, int(i) % w.Hkv) for i in sorted(idx)]
 
 
 def test_attn_full_c1():
@@ -353,13 +378,20 @@ def test_attn_full_c2():
 
 
 def test_attn_full_c3():
-    _full("c3", lambda w, lens: [(0, 0), (31, 5), (63, 7)])
+    """32 seeded random (sequence, kv head) groups of 512, plus the corners."""
+    _full("c3", lambda w, lens: sorted({(0, 0), (63, 7)} | set(_random_groups(w, 32, 3003))))
 
 
 def test_attn_full_c4():
+    """Every kv head of sequences 0..12 (the 13 forced unaligned lengths
+    1 ... 16384, one shard each), the last sequence with an empty shard,
+    and 32 seeded random groups of 2048."""
     def groups(w, lens):
+        forced = {(b, h) for b in range(len(sc.EDGE_LENGTHS)) for h in range(w.Hkv)}
+        for i, e in enumerate(sc.EDGE_LENGTHS):
+            assert lens[i % w.R, i] == e
         empty_b = int(np.where((lens == 0).any(axis=0))[0][-1])
-        return [(0, 0), (11, 3), (12, 7), (empty_b, 2)]
+        return sorted(forced | {(empty_b, 2)} | set(_random_groups(w, 32, 3004)))
     _full("c4", groups)
 
 

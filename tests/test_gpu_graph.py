@@ -1,12 +1,15 @@
 """HIP-graph replay of a whole step (partial attention + merge) gives the
 eager result bit for bit on every replay, with eager work and
-synchronisations between replays (the path records no memset nodes)."""
+synchronisations between replays (the path records no memset nodes), and
+every replay meets the oracle."""
 import sys
 
+import numpy as np
 import pytest
 
+from oracle import workloads as ow
 from synth import configs as sc
-from tests.helpers import run_path
+from tests.helpers import assert_lse, assert_out, run_path, to64
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -71,6 +74,29 @@ def test_graph_replay_matches_eager(name, w):
         outs = [o_part, lse_part, out, lo]
         refs = [ref["o_part"], ref["lse_part"], ref["out"], ref["lse_out"]]
         eager_work = lambda: run_path(inp)
+    if w is None:
+        rows = np.unique(np.concatenate([np.arange(0, wm.rows, 17),
+                                         np.where(np.isneginf(inp["lse_np"]).any(axis=0))[0][:64]]))
+        o_ref, lo_ref = ow.merge_rows(wm, rows)
+
+        def check_oracle(rep):
+            assert_out(to64(out[rows]), o_ref, f"replay {rep} merge out")
+            assert_lse(to64(lo[rows]), lo_ref, f"replay {rep} merge lse_out")
+    else:
+        groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+        if len(groups) > 48:   # larger cases: 48 seeded random groups
+            pick = np.random.default_rng(77).choice(len(groups), size=48, replace=False)
+            groups = [groups[i] for i in sorted(pick)]
+        grefs = {g: ow.group(w, inp["lens_np"], *g) for g in groups}
+        o_part_t, _, out_t, lo_t = outs
+
+        def check_oracle(rep):
+            for (b, h), ref in grefs.items():
+                hs = slice(h * w.G, (h + 1) * w.G)
+                assert_out(to64(out_t[b, hs]), ref["out"], f"replay {rep} out b={b} h={h}")
+                assert_lse(to64(lo_t[b, hs]), ref["lse_out"], f"replay {rep} lse_out b={b} h={h}",
+                           floor=True)
+                assert_out(to64(o_part_t[:, b, hs]), ref["o_part"], f"replay {rep} o_part b={b} h={h}")
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -89,5 +115,6 @@ def test_graph_replay_matches_eager(name, w):
         torch.cuda.synchronize()
         for t, r in zip(outs, refs):
             assert torch.equal(t, r), f"replay {rep}: output differs from eager"
+        check_oracle(rep)
         eager_work()
         torch.cuda.synchronize()

@@ -243,7 +243,7 @@ def test_step_on_two_streams_with_binding_workspaces():
         outs[name] = res
         calls[name] = cp.StepCall(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"],
                                   res["o_part"], res["lse_part"], res["out"], res["lse_out"], stream=s)
-    assert calls["a"]._keep[6].data_ptr() != calls["b"]._keep[6].data_ptr()
+    assert calls["a"].workspace(sa).data_ptr() != calls["b"].workspace(sb).data_ptr()
     torch.cuda.synchronize()
     for _ in range(20):
         calls["a"](sa.cuda_stream)
@@ -252,4 +252,35 @@ def test_step_on_two_streams_with_binding_workspaces():
     for name, ref in (("a", ref_a), ("b", ref_b)):
         for k in ref:
             assert torch.equal(outs[name][k], ref[k]), f"stream {name}: {k} differs"
-        assert counters_zero(calls[name]._keep[6])
+        assert counters_zero(calls[name].workspace(sa if name == "a" else sb))
+
+
+def test_step_on_new_streams_without_synchronisation():
+    """The binding's workspace for a stream is allocated and zero-filled on
+    that stream, so a call made for a new stream may run at once, with no
+    synchronisation between making the call and running it: on fresh
+    streams, a small shape first and then a larger one (whose workspace
+    replaces the smaller one of the same stream) give the single-stream
+    results bit for bit, through the marshalled calls and through the
+    one-shot functions alike."""
+    _say("step on new streams, no synchronisation")
+    small_w, big_w = sc.WORKLOADS["c1"], sc.small("c4", B=2, Hq=16, Lcap=1024)
+    si, bi = sg.attn_inputs(small_w), sg.attn_inputs(big_w)
+    ref_s, ref_b = run_step(si), run_step(bi)
+    for rep in range(3):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())   # inputs are ready before s runs
+        got_s = {k: torch.empty_like(v) for k, v in ref_s.items()}
+        got_b = {k: torch.empty_like(v) for k, v in ref_b.items()}
+        call = cp.StepCall(si["q"], si["k_shards"], si["v_shards"], si["lens"], got_s["o_part"],
+                           got_s["lse_part"], got_s["out"], got_s["lse_out"], stream=s)
+        call(s.cuda_stream)
+        # the larger shape on the same stream: a larger workspace replaces the first
+        cp.cp_decode(bi["q"], bi["k_shards"], bi["v_shards"], bi["lens"], got_b["o_part"],
+                     got_b["lse_part"], got_b["out"], got_b["lse_out"], stream=s)
+        for t in (*got_s.values(), *got_b.values()):
+            t.record_stream(s)
+        s.synchronize()
+        for k in ref_s:
+            assert torch.equal(got_s[k], ref_s[k]), f"rep {rep}: small shape {k} differs"
+            assert torch.equal(got_b[k], ref_b[k]), f"rep {rep}: larger shape {k} differs"
