@@ -16,6 +16,8 @@
  * Conventions shared by every entry point
  *   - Plain C ABI.  All tensors are caller-owned device pointers; the library
  *     never allocates, frees or synchronises, and keeps no per-call state.
+ *     Its only device state is the static scratch array of
+ *     cpdec_cp_decode_noalloc (one per GPU, part of the loaded library).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     CPDEC_OK means the work was enqueued on that stream; device faults
  *     surface at the caller's next synchronisation.
@@ -290,6 +292,37 @@ cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
                              void* o_part, float* lse_part, void* out,
                              float* lse_out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * cpdec_cp_decode for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same step, kernels and results (bit for bit), but its
+ * scratch (arrival counters, chunk partials, launch order) lives in a
+ * static device array of CPDEC_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends.  The caller passes inputs and
+ * outputs only; nothing is allocated or freed, by the library or for it.
+ *
+ * The first call on a device looks up that GPU's array (the device current
+ * at the call) and clears its counter region with a kernel on `stream`;
+ * every completed call leaves the counters zero again, and the rest of the
+ * array is overwritten before it is read.  Every call on one GPU shares the
+ * array: two calls that may overlap in time on the same GPU (other streams,
+ * other threads) race on it and must be serialised by the caller, e.g. by
+ * issuing them on one stream.
+ *
+ *   d, q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out, stream
+ *              as for cpdec_cp_decode
+ * Errors: as cpdec_cp_decode (checked before any HIP call); WORKSPACE when
+ * the step needs more scratch than CPDEC_NOALLOC_SCRATCH_BYTES
+ * (cpdec_step_workspace_bytes(d) tells how much it needs); HIP when the
+ * array cannot be reached on the current device.
+ */
+#define CPDEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+cpdec_status cpdec_cp_decode_noalloc(const cpdec_attn_desc* d, const void* q,
+                                     const void* const* k_shards,
+                                     const void* const* v_shards, const int32_t* lens,
+                                     void* o_part, float* lse_part, void* out,
+                                     float* lse_out, void* stream);
 
 /*
  * Zero-fill `bytes` bytes of a buffer on `stream` with a kernel (no

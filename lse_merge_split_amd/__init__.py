@@ -14,10 +14,11 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "StepCall", "attn_partial",
+__all__ = ["lib", "AttnDesc", "CpdecError", "AttnCall", "MergeCall", "StepCall",
+           "StepCallNoAlloc", "attn_partial",
            "lse_merge", "cp_decode", "attn_workspace_bytes", "step_workspace_bytes", "attn_plan",
            "step_launches", "workspace_clear", "make_attn_desc", "DTYPE_CODES", "STATUS",
-           "STEP_COUNTER_BYTES"]
+           "STEP_COUNTER_BYTES", "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpdec.so")
@@ -26,6 +27,7 @@ STATUS = {0: "CPDEC_OK", 1: "CPDEC_ERR_INVALID_ARG", 2: "CPDEC_ERR_UNSUPPORTED",
           3: "CPDEC_ERR_ALIGNMENT", 4: "CPDEC_ERR_WORKSPACE", 5: "CPDEC_ERR_HIP"}
 F32, F16, BF16 = 0, 1, 2
 STEP_COUNTER_BYTES = 65536  # CPDEC_STEP_COUNTER_BYTES: counter region at the workspace start
+NOALLOC_SCRATCH_BYTES = 16 << 20  # CPDEC_NOALLOC_SCRATCH_BYTES: cpdec_cp_decode_noalloc's scratch
 
 
 class CpdecError(RuntimeError):
@@ -75,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.cpdec_cp_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
                                       ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, sz, vp]
         L.cpdec_cp_decode.restype = ctypes.c_int
+        L.cpdec_cp_decode_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp, ctypes.POINTER(vp),
+                                              ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp]
+        L.cpdec_cp_decode_noalloc.restype = ctypes.c_int
         L.cpdec_lse_merge.argtypes = [vp, vp, i32, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.cpdec_lse_merge.restype = ctypes.c_int
         L.cpdec_workspace_clear.argtypes = [vp, sz, vp]
@@ -342,6 +347,28 @@ class StepCall(AttnCall):
         self._outs = self._outs + [out.data_ptr(),
                                    lse_out.data_ptr() if lse_out is not None else None]
         self.launches = step_launches(desc)
+
+
+class StepCallNoAlloc(StepCall):
+    """A cpdec_cp_decode_noalloc call: the whole step with the library's own
+    static scratch (one per GPU, shared by every such call on it: calls that
+    may overlap on one GPU must be serialised by the caller).  No workspace
+    is allocated for it; a step that needs more scratch than
+    NOALLOC_SCRATCH_BYTES raises CpdecError (CPDEC_ERR_WORKSPACE)."""
+
+    _entry = "cpdec_cp_decode_noalloc"
+
+    def __init__(self, q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, **kw):
+        if kw.get("workspace") is not None:
+            raise ValueError("cpdec_cp_decode_noalloc takes no workspace")
+        super().__init__(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out, **kw)
+
+    def _args_for(self, stream: int):
+        args = self._by_stream.get(stream)
+        if args is None:
+            args = (self._head + self._outs, None)
+            self._by_stream[stream] = args
+        return args
 
 
 def cp_decode(q, k_shards, v_shards, lens, o_part, lse_part, out, lse_out=None, *, stream=None,

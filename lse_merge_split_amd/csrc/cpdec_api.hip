@@ -5,10 +5,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "cpdec.h"
 #include "kernels.h"
 
 static_assert(cpdec::kStepCounterBytes == CPDEC_STEP_COUNTER_BYTES, "counter region size");
+
+// Scratch of cpdec_cp_decode_noalloc: one copy per GPU, held until the
+// process ends, shared by every call on that GPU.  In host code this name is
+// only a stand-in for the symbol; the device address of each GPU's copy comes
+// from hipGetSymbolAddress (scratch_for_current_device below) and is the only
+// thing host code passes on.
+static __device__ __align__(256) unsigned char scratch[CPDEC_NOALLOC_SCRATCH_BYTES];
+static_assert(CPDEC_NOALLOC_SCRATCH_BYTES >= CPDEC_STEP_COUNTER_BYTES, "scratch holds the counters");
 
 namespace {
 
@@ -303,6 +313,30 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
 
 size_t dtype_size(int dt) { return dt == CPDEC_F32 ? 4 : 2; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  The first lookup on a device
+// also clears the arrival counters at the start of the scratch on `stream`,
+// ahead of the kernels that use them; every completed call leaves them zero.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices] = {};
+
+cpdec_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CPDEC_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return CPDEC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return CPDEC_ERR_HIP;
+    if (launch_clear(ptr, kStepCounterBytes, stream) != hipSuccess) return CPDEC_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return CPDEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,7 +410,7 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
                                 const void* const* k_shards, const void* const* v_shards,
                                 const int32_t* lens, void* o_part, float* lse_part,
                                 void* workspace, size_t workspace_bytes, const StepOut* so,
-                                void* stream);
+                                void* stream, bool use_scratch = false);
 
 cpdec_status cpdec_attn_partial(const cpdec_attn_desc* d, const void* q,
                                 const void* const* k_shards, const void* const* v_shards,
@@ -398,11 +432,22 @@ cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
                      workspace_bytes, &so, stream);
 }
 
+cpdec_status cpdec_cp_decode_noalloc(const cpdec_attn_desc* d, const void* q,
+                                     const void* const* k_shards, const void* const* v_shards,
+                                     const int32_t* lens, void* o_part, float* lse_part,
+                                     void* out, float* lse_out, void* stream) {
+  if (out == nullptr) return CPDEC_ERR_INVALID_ARG;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return CPDEC_ERR_ALIGNMENT;
+  StepOut so{out, lse_out, d != nullptr ? (int)d->qkv_dtype : 0};
+  return attn_launch(d, q, k_shards, v_shards, lens, o_part, lse_part, nullptr, 0, &so, stream,
+                     true);
+}
+
 static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
                                 const void* const* k_shards, const void* const* v_shards,
                                 const int32_t* lens, void* o_part, float* lse_part,
                                 void* workspace, size_t workspace_bytes, const StepOut* so,
-                                void* stream) {
+                                void* stream, bool use_scratch) {
   AttnPlan pl;
   cpdec_status st = plan_attn(d, &pl);
   if (st != CPDEC_OK) return st;
@@ -425,7 +470,13 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
       return CPDEC_ERR_UNSUPPORTED;
   }
   const size_t need = so != nullptr ? pl.step_ws_bytes : pl.ws_bytes;
-  if (need > 0) {
+  if (use_scratch) {
+    // the library's own scratch: every check above ran without a HIP call
+    if (need > CPDEC_NOALLOC_SCRATCH_BYTES) return CPDEC_ERR_WORKSPACE;
+    const cpdec_status sst = scratch_for_current_device(static_cast<hipStream_t>(stream), &workspace);
+    if (sst != CPDEC_OK) return sst;
+    workspace_bytes = CPDEC_NOALLOC_SCRATCH_BYTES;
+  } else if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
       return CPDEC_ERR_WORKSPACE;

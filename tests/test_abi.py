@@ -259,6 +259,34 @@ def test_cp_decode_errors():
 
 
 @needs_cpu_host
+def test_cp_decode_noalloc_errors():
+    """The allocation-free step checks everything before its first HIP call
+    (the scratch lookup): argument errors as cpdec_cp_decode, and WORKSPACE
+    for a step that needs more than CPDEC_NOALLOC_SCRATCH_BYTES."""
+    f = cp.lib().cpdec_cp_decode_noalloc
+    d = _desc(chunk_tokens=1024)
+    ks = (ctypes.c_void_p * 4)(*([A] * 4))
+    assert f(None, A, ks, ks, A, A, A, A, A, None) == INVALID
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, None, A, None) == INVALID
+    assert f(ctypes.byref(d), None, ks, ks, A, A, A, A, A, None) == INVALID
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A + 8, A, None) == ALIGN
+    assert f(ctypes.byref(d), A, ks, ks, A, A, A, A, A + 2, None) == ALIGN
+    assert f(ctypes.byref(_desc(chunk_tokens=1024, head_dim=96)), A, ks, ks, A, A, A, A, A,
+             None) == UNSUPPORTED
+    # 8 shards x 16 heads at D = 256 in 256 chunks of 32 tokens: 33.8 MB of chunk partials
+    big = _desc(batch=1, num_q_heads=16, num_kv_heads=1, head_dim=256, num_shards=8,
+                kv_capacity=8192, kv_stride_token=256, kv_stride_head=8192 * 256,
+                kv_stride_batch=8192 * 256, chunk_tokens=32)
+    assert cp.step_workspace_bytes(big) > cp.NOALLOC_SCRATCH_BYTES
+    ks8 = (ctypes.c_void_p * 8)(*([A] * 8))
+    assert f(ctypes.byref(big), A, ks8, ks8, A, A, A, A, A, None) == WS
+    # the scratch size the header states is the one the binding assumes
+    txt = open(os.path.join(ROOT, "include", "cpdec.h")).read()
+    assert "#define CPDEC_NOALLOC_SCRATCH_BYTES (16u << 20)" in txt
+    assert cp.NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+@needs_cpu_host
 def test_merge_errors():
     m = cp.lib().cpdec_lse_merge
     assert m(None, A, 4, 10, 128, cp.BF16, cp.BF16, A, A, None) == INVALID
