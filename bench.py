@@ -184,18 +184,34 @@ def time_workload(name: str, K: int, W: int, torch, cp, sg, fused: bool = True,
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    # Steps of a millisecond or more also get an event pair each (an event
+    # record costs a few microseconds of device time, negligible there), for
+    # the spread of the step time; shorter steps are timed by the span alone.
+    per_step = alg_attn + alg_merge >= (4 << 30)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)] \
+        if per_step else None
     edge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     edge[0].record()
     for i in range(K):
+        if evs:
+            evs[i][0].record()
         step(i)
+        if evs:
+            evs[i][1].record()
     edge[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"[bench] {w.name}: timed {K} steps", file=sys.stderr, flush=True)
     us_per_call = (t1 - t0) / K * 1e6
     device_us = edge[0].elapsed_time(edge[1]) * 1e3 / K
+    spread = None
+    if evs:
+        ts = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        spread = {"p10": round(float(np.percentile(ts, 10)), 1),
+                  "median": round(float(np.median(ts)), 1),
+                  "p90": round(float(np.percentile(ts, 90)), 1)}
 
     if w.merge_only:
         step_bytes = alg_merge
@@ -226,6 +242,8 @@ def time_workload(name: str, K: int, W: int, torch, cp, sg, fused: bool = True,
         "device_us_per_call": round(device_us, 3),
         "effective_GBps": round(step_bytes / (us_per_call * 1e-6) / 1e9, 1),
     }
+    if spread:
+        block["step_us_events"] = spread
 
     if graph:
         # One graph per input copy, replayed in the same rotation as the eager
@@ -481,6 +499,23 @@ def main():
         ke, we = EXTRA_STEPS.get(e, (20, 5))
         extra_blocks[e] = time_workload(e, ke, we, torch, cp, sg, graph=(e in ("c1", "c2")))
 
+    # Context for the roofline: a plain 1 GiB device-to-device copy on this GPU
+    # (read + write bytes over its time), the attainable rate of a simple stream.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record()
+    for _ in range(10):
+        dst.copy_(src)
+    ce[1].record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -509,6 +544,8 @@ def main():
         "cpu_baseline": cpu,
         "device_us_per_call": head["device_us_per_call"],
         "effective_GBps": head["effective_GBps"],
+        "step_us_events": head.get("step_us_events"),
+        "d2d_copy_GBps": round(copy_gbps, 1),
         "kernel_source_hash": kernel_source_hash(),
     }
     for k in ("graph_us_per_call", "graph_device_us_per_call", "graph_all_steps_device_us_per_call",

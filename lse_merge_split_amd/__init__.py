@@ -192,8 +192,10 @@ def _workspace(device, nbytes, stream=None):
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
         current = torch.cuda.current_stream(device)
-        target = current if current.cuda_stream == stream else \
-            torch.cuda.ExternalStream(stream, device=device)
+        default = torch.cuda.default_stream(device)
+        target = (current if current.cuda_stream == stream else
+                  default if default.cuda_stream == stream else
+                  torch.cuda.ExternalStream(stream, device=device))
         with torch.cuda.stream(target):
             ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS_CACHE[key] = ws

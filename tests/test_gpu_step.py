@@ -94,6 +94,9 @@ def counters_zero(ws):
 
 
 def check_against_oracle(w, inp, res, what):
+    # the five workloads at full size hold the merged lse to the strict 1e-5
+    # relative bar; reduced and random shapes may cancel towards 0 (floor)
+    full = w.name in sc.WORKLOADS and w == sc.WORKLOADS[w.name]
     for b in range(w.B):
         for h in range(w.Hkv):
             ref = ow.group(w, inp["lens_np"], b, h)
@@ -102,7 +105,8 @@ def check_against_oracle(w, inp, res, what):
             assert_lse(to64(res["lse_part"][:, b, hs]), ref["lse_part"], f"{what} lse_part b={b} h={h}",
                        floor=True)
             assert_out(to64(res["out"][b, hs]), ref["out"], f"{what} out b={b} h={h}")
-            assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}", floor=True)
+            assert_lse(to64(res["lse_out"][b, hs]), ref["lse_out"], f"{what} lse_out b={b} h={h}",
+                       floor=not full)
 
 
 @pytest.mark.parametrize("name", list(CASES))
