@@ -10,8 +10,10 @@
  * The program sizes one workspace for both attention entry points, clears it
  * once, runs cpdec_cp_decode twice on it (the counter region must be zero
  * after each call), then cpdec_attn_partial + cpdec_lse_merge into a second
- * set of outputs, and writes {o_part fp32, lse_part, out 16-bit, lse_out} of
- * the first call, of the second call and of the two-call form to outputs.bin. */
+ * set of outputs, then cpdec_cp_decode_noalloc (no workspace) into a third,
+ * and writes {o_part fp32, lse_part, out 16-bit, lse_out} of the first call,
+ * of the second call, of the two-call form and of the allocation-free step
+ * to outputs.bin. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -136,10 +138,11 @@ int main(int argc, char** argv) {
 
   const size_t n_opart = (size_t)R * B * Hq * D, n_lsep = (size_t)R * B * Hq;
   const size_t n_out = (size_t)B * Hq * D, n_lse = (size_t)B * Hq;
-  outputs step1, step2, two;
+  outputs step1, step2, two, na;
   if (alloc_outputs(&step1, n_opart, n_lsep, n_out, n_lse) ||
       alloc_outputs(&step2, n_opart, n_lsep, n_out, n_lse) ||
-      alloc_outputs(&two, n_opart, n_lsep, n_out, n_lse))
+      alloc_outputs(&two, n_opart, n_lsep, n_out, n_lse) ||
+      alloc_outputs(&na, n_opart, n_lsep, n_out, n_lse))
     return 1;
 
   // one workspace serves both attention entry points
@@ -169,12 +172,17 @@ int main(int argc, char** argv) {
                             d.qkv_dtype, two.out, two.lse_out, s));
   HIP_OK(hipStreamSynchronize(s));
   if (!zero1 || !zero2) { fprintf(stderr, "counter region not zero after a call\n"); return 1; }
+  // the same step with the library's static scratch: no workspace from the caller
+  CPDEC_OK_(cpdec_cp_decode_noalloc(&d, q, ks, vs, lens, na.o_part, na.lse_part, na.out,
+                                    na.lse_out, s));
+  HIP_OK(hipStreamSynchronize(s));
 
   FILE* fout = fopen(argv[2], "wb");
   if (!fout) { perror(argv[2]); return 1; }
   if (write_outputs(fout, &step1, n_opart, n_lsep, n_out, n_lse) ||
       write_outputs(fout, &step2, n_opart, n_lsep, n_out, n_lse) ||
-      write_outputs(fout, &two, n_opart, n_lsep, n_out, n_lse)) {
+      write_outputs(fout, &two, n_opart, n_lsep, n_out, n_lse) ||
+      write_outputs(fout, &na, n_opart, n_lsep, n_out, n_lse)) {
     fprintf(stderr, "writing outputs failed\n");
     return 1;
   }

@@ -3,9 +3,11 @@ the C ABI with device buffers from the HIP runtime's C API, no Python
 binding and no torch on the GPU side.
 
 The test writes seeded inputs (K/V padding past each length filled with
-NaN), the program runs cpdec_cp_decode twice on one workspace and the two
-calls cpdec_attn_partial + cpdec_lse_merge, and every output is checked
-against the oracle; the repeat call must reproduce the first bit for bit.
+NaN), the program runs cpdec_cp_decode twice on one workspace, the two
+calls cpdec_attn_partial + cpdec_lse_merge and the allocation-free
+cpdec_cp_decode_noalloc, and every output is checked against the oracle; the
+repeat call and the allocation-free step must reproduce the first call bit
+for bit.
 """
 import os
 import shutil
@@ -105,6 +107,7 @@ def test_c_caller(name, step_c, tmp_path):
     step1, at = _unpack(buf, R, B, Hq, D, dt, 0)
     step2, at = _unpack(buf, R, B, Hq, D, dt, at)
     two, at = _unpack(buf, R, B, Hq, D, dt, at)
+    na, at = _unpack(buf, R, B, Hq, D, dt, at)
     assert at == len(buf)
 
     o_ref, lp_ref, out_ref, lo_ref = orc.cp_decode(q64, list(k64), list(v64), lens, Hkv)
@@ -115,3 +118,4 @@ def test_c_caller(name, step_c, tmp_path):
         assert_lse(res["lse_part"], lp_ref, f"{what} lse_part", floor=True)
     for k in step1:
         assert np.array_equal(step1[k], step2[k], equal_nan=False), f"repeat call: {k} differs"
+        assert np.array_equal(step1[k], na[k], equal_nan=False), f"allocation-free step: {k} differs"
