@@ -302,8 +302,9 @@ cpdec_status cpdec_cp_decode(const cpdec_attn_desc* d, const void* q,
  * one per GPU, held until the process ends.  The caller passes inputs and
  * outputs only; nothing is allocated or freed, by the library or for it.
  *
- * The first call on a device looks up that GPU's array (the device current
- * at the call) and clears its counter region with a kernel on `stream`;
+ * The first call on a device looks up that GPU's array (the device `stream`
+ * belongs to; the current device for the null stream) and clears its counter
+ * region with a kernel on `stream`;
  * every completed call leaves the counters zero again, and the rest of the
  * array is overwritten before it is read.  Every call on one GPU shares the
  * array: two calls that may overlap in time on the same GPU (other streams,

@@ -15,7 +15,7 @@ static_assert(cpdec::kStepCounterBytes == CPDEC_STEP_COUNTER_BYTES, "counter reg
 // Scratch of cpdec_cp_decode_noalloc: one copy per GPU, held until the
 // process ends, shared by every call on that GPU.  In host code this name is
 // only a stand-in for the symbol; the device address of each GPU's copy comes
-// from hipGetSymbolAddress (scratch_for_current_device below) and is the only
+// from hipGetSymbolAddress (scratch_for_stream below) and is the only
 // thing host code passes on.
 static __device__ __align__(256) unsigned char scratch[CPDEC_NOALLOC_SCRATCH_BYTES];
 static_assert(CPDEC_NOALLOC_SCRATCH_BYTES >= CPDEC_STEP_COUNTER_BYTES, "scratch holds the counters");
@@ -313,24 +313,33 @@ cpdec_status plan_attn(const cpdec_attn_desc* d, AttnPlan* pl) {
 
 size_t dtype_size(int dt) { return dt == CPDEC_F32 ? 4 : 2; }
 
-// Device address of `scratch` on the current device, looked up once per
-// device (with that device current) and kept.  The first lookup on a device
-// also clears the arrival counters at the start of the scratch on `stream`,
-// ahead of the kernels that use them; every completed call leaves them zero.
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream), looked up once per device with that
+// device current and kept.  The first lookup on a device also clears the
+// arrival counters at the start of the scratch on `stream`, ahead of the
+// kernels that use them; every completed call leaves them zero.
 constexpr int kScratchDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch[kScratchDevices] = {};
 
-cpdec_status scratch_for_current_device(hipStream_t stream, void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return CPDEC_ERR_HIP;
+cpdec_status scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return CPDEC_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return CPDEC_ERR_HIP;
+    dev = (int)sd;
+  }
   if (dev < 0 || dev >= kScratchDevices) return CPDEC_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return CPDEC_ERR_HIP;
     void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
-      return CPDEC_ERR_HIP;
-    if (launch_clear(ptr, kStepCounterBytes, stream) != hipSuccess) return CPDEC_ERR_HIP;
+    const bool found = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr;
+    const bool cleared = found && launch_clear(ptr, kStepCounterBytes, stream) == hipSuccess;
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return CPDEC_ERR_HIP;
+    if (!cleared) return CPDEC_ERR_HIP;
     g_scratch[dev] = ptr;
   }
   *out = g_scratch[dev];
@@ -473,7 +482,7 @@ static cpdec_status attn_launch(const cpdec_attn_desc* d, const void* q,
   if (use_scratch) {
     // the library's own scratch: every check above ran without a HIP call
     if (need > CPDEC_NOALLOC_SCRATCH_BYTES) return CPDEC_ERR_WORKSPACE;
-    const cpdec_status sst = scratch_for_current_device(static_cast<hipStream_t>(stream), &workspace);
+    const cpdec_status sst = scratch_for_stream(static_cast<hipStream_t>(stream), &workspace);
     if (sst != CPDEC_OK) return sst;
     workspace_bytes = CPDEC_NOALLOC_SCRATCH_BYTES;
   } else if (need > 0) {
