@@ -233,7 +233,8 @@ def time_workload(name: str, K: int, W: int, torch, cp, sg, fused: bool = True,
                    "rows": w.rows or None, "input_copies": info["copies"],
                    "chunk_tokens": info.get("chunk"), "chunks_per_shard": info.get("nchunks"),
                    "waves_per_workgroup": info.get("waves"),
-                   "longest_first": info.get("longest_first"), "parallelism": "single GPU"},
+                   "longest_first": info.get("longest_first"), "seed": w.seed,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kernels_of(w, fused, info),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
