@@ -971,9 +971,12 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
 // nchp), nchp = chunks rounded up to a power of two), so every statistic is
 // an xor-shuffle reduction; threads (partition, shard, float4) sum their
 // chunk vectors from registers.  Same formulas as merge_chunks (chunk max,
-// weights, shard lse; FP64 cross-shard weights and lse), with the shuffle
-// trees' summation order.  Needs R * Q <= threads and every live chunk among
-// the 16 * P a thread group loads (both hold where it is called).
+// weights, shard lse; cross-shard weights; merged lse in FP64), with the
+// shuffle trees' summation order, except that the cross-shard weights that
+// scale the output are FP32 here (the output moves by ~1e-7 of itself, far
+// inside its tolerance) so that the FP64 merged lse can be formed beside the
+// output instead of ahead of it.  Needs R * Q <= threads and every live chunk
+// among the 16 * P a thread group loads (both hold where it is called).
 template <int D, int NW, int MODE>
 __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, const int* s_nl,
                                  MergeSmem<NW, MODE>& ms, int lg_nchp) {
@@ -1040,12 +1043,17 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
     const float ls = S > 0.f ? M + logf(S) : neg_inf();  // shard lse (nl == 1: the stored one)
     if (nll >= 2 && cl == 0) p.lse_part[rl * rstride + row0] = ls;
     const float Mx = wave_max(cl == 0 ? ls : neg_inf());  // max over shards
-    const double ew = (cl == 0 && rl < R && ls != neg_inf()) ? exp((double)ls - (double)Mx) : 0.0;
-    const double St = wave_sum_f64(ew);
-    if (cl == 0 && rl < R) ms.lse[rl] = (float)ew;  // shard weight (unnormalised)
+    // FP32 cross-shard weights for the output; the merged lse is formed in
+    // FP64 at the end, off the path to the output.
+    const float ew = (cl == 0 && rl < R && ls != neg_inf()) ? expf(ls - Mx) : 0.f;
+    const float St = wave_sum(ew);
+    if (cl == 0 && rl < R) {
+      ms.lse[rl] = ew;               // shard weight (unnormalised)
+      ms.lse[kMaxShards + rl] = ls;  // shard lse, for the merged lse
+    }
     if (lane == 0) {
-      ms.M[0] = St > 0.0 ? (float)(1.0 / St) : 0.f;
-      if (p.lse_out != nullptr) p.lse_out[row0] = St > 0.0 ? (float)((double)Mx + log(St)) : neg_inf();
+      ms.M[0] = St > 0.f ? 1.0f / St : 0.f;
+      ms.M[1] = Mx;
     }
   }
   __syncthreads();
@@ -1091,6 +1099,17 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
 #pragma unroll 4
     for (int r = 0; r < R; ++r) acc += ms.lse[r] * ms.y[r * Q + t];
     store4(p.out, (int64_t)row0 * D + 4 * t, acc * ms.M[0], p.out_dt);
+  }
+  // ---- (5) merged lse, FP64 (the merge kernel's formula) ----
+  // Lane r of the last wave takes shard r (R <= 64 here), so with two or more
+  // waves this runs beside the output above instead of ahead of it.
+  if (p.lse_out != nullptr && (t >> 6) == NW - 1) {
+    const int r = t & 63;
+    const float Mx = ms.M[1];
+    const float ls = r < R ? ms.lse[kMaxShards + r] : neg_inf();
+    const double e = ls != neg_inf() ? exp((double)ls - (double)Mx) : 0.0;
+    const double St = wave_sum_f64(e);
+    if (r == 0) p.lse_out[row0] = St > 0.0 ? (float)((double)Mx + log(St)) : neg_inf();
   }
 }
 
