@@ -975,15 +975,15 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
 // shuffle trees' summation order, except that the cross-shard weights that
 // scale the output are FP32 here (the output moves by ~1e-7 of itself, far
 // inside its tolerance) so that the FP64 merged lse can be formed beside the
-// output instead of ahead of it.  Needs R * Q <= threads and every live chunk
-// among the 16 * P a thread group loads (both hold where it is called).
-template <int D, int NW, int MODE>
+// output instead of ahead of it.  KB chunk vectors are loaded per thread
+// group.  Needs R * Q <= threads and every live chunk among the KB * P a
+// thread group loads (both hold where it is called).
+template <int D, int NW, int MODE, int KB = 16>
 __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, const int* s_nl,
                                  MergeSmem<NW, MODE>& ms, int lg_nchp) {
   constexpr int NT = NW * 64;
   constexpr int Q = D / 4;
   constexpr int LGQ = __builtin_ctz(Q);
-  constexpr int KB = 16;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int R = p.R;
@@ -1113,6 +1113,7 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
   }
 }
 
+
 // One arrival at a counter of `members` arrivals (relaxed, agent scope; the
 // caller's device-scope stores have completed).  Returns whether this was the
 // last arrival, and then resets the counter to zero for the next call.
@@ -1225,7 +1226,10 @@ __device__ void combine_unit(const Args& p, int unit, int r, int b, int h, int g
   }
 }
 
-template <typename T, int D, int NW, int MODE, bool ORDERED = false, bool SPEC2 = false>
+// SMALL_MERGE: the one-launch single-head merge loads 2 chunk vectors per
+// thread group instead of 16 (the launch checks that 2 cover every chunk).
+template <typename T, int D, int NW, int MODE, bool ORDERED = false, bool SPEC2 = false,
+          bool SMALL_MERGE = false>
 __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams kp) {
   const void* kshard;
   const void* vshard;
@@ -1328,7 +1332,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnParams 
         int lg_nchp = 0;
         while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
         if (p.G == 1 && (p.R << lg_nchp) <= 64)
-          merge_row_chunks<D, NW>(p, b, h, 0, 0, s_nl, sh.m, lg_nchp);
+          merge_row_chunks<D, NW, MODE, SMALL_MERGE ? 2 : 16>(p, b, h, 0, 0, s_nl, sh.m, lg_nchp);
         else
           merge_chunks<D, NW>(p, b, h, gb, s_nl, sh.m);
       }
@@ -1514,6 +1518,23 @@ hipError_t launch_order(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Whether the one-launch step's merge takes the single-head merger with 2
+// chunk vectors per thread group: one query head per group (G = 1), shards x
+// chunks (rounded up to a power of two) within one wave, and ceil(chunks /
+// partitions) <= 2, where partitions = threads / (R * D/4 rounded up to a
+// power of two, at least D/4) -- as merge_row_chunks lays them out.
+inline bool small_row_merge(const AttnParams& p, int D, int NW) {
+  if (p.G != 1) return false;
+  int lg_nchp = 0;
+  while ((1 << lg_nchp) < p.nchunks) ++lg_nchp;
+  if ((p.R << lg_nchp) > 64) return false;
+  const int q = D / 4;
+  int per = q;
+  while (per < p.R * q) per <<= 1;
+  const int parts = NW * 64 / per;
+  return parts >= 1 && (p.nchunks + parts - 1) / parts <= 2;
+}
+
 template <typename T, int D, int NW>
 hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipStream_t s) {
   const dim3 grid((unsigned)(units / p.R * p.nchunks), (unsigned)p.R), block(NW * 64);
@@ -1531,6 +1552,20 @@ hipError_t launch_typed(const AttnParams& p, int64_t units, StepMode mode, hipSt
     return hipGetLastError();
   }
   if (mode == kStepOneChunks) {
+    // Single-head groups whose chunks 2 loads per merging thread group cover
+    // take the kernel with the short merge (c1: 7.80 -> 7.48 us); a second
+    // merge inside one kernel made the longer splits slower (c2 +0.25 us).
+    if constexpr (NW == 2 || NW == 4) {
+      if (small_row_merge(p, D, NW)) {
+        if (p.chunk >= 2 * NW * kTileTokens)
+          hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks, false, true, true>), grid,
+                             block, 0, s, p);
+        else
+          hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks, false, false, true>), grid,
+                             block, 0, s, p);
+        return hipGetLastError();
+      }
+    }
     // two or more tiles per wave: request the second tile with the first
     if (p.chunk >= 2 * NW * kTileTokens)
       hipLaunchKernelGGL((attn_partial_kernel<T, D, NW, kStepOneChunks, false, true>), grid, block, 0,
