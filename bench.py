@@ -12,8 +12,9 @@ region starts.
 The headline workload (default c4: 8 shards, batch 256, 64/8 heads, D=128,
 ragged lengths, the largest one-GPU workload) is timed for exactly --steps
 steps after --warmup untimed ones.  The other large workloads (c3, the
-merge-only c5) and the small c2 with its HIP-graph replay are then timed in
-the same process, each in a block of its own (--extras; "none" skips them).
+merge-only c5) and the small c2 and c1, each with its HIP-graph replay, are
+then timed in the same process, each in a block of its own (--extras; "none"
+skips them).
 
 Prints ONE JSON line:
   value          eager microseconds per call (wall clock of K back-to-back
@@ -453,9 +454,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", choices=sorted(sc.WORKLOADS),
                     help="headline workload (default c4, the largest one-GPU workload)")
-    ap.add_argument("--extras", default="c3,c5,c2",
+    ap.add_argument("--extras", default="c3,c5,c2,c1",
                     help="other workloads timed after the headline, each in a block of its own "
-                         "(c2's block includes its HIP-graph replay); 'none' for none")
+                         "(the c2 and c1 blocks include their HIP-graph replay); 'none' for none")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0,
                     help="seconds of oracle work per host process for cpu_baseline (0 disables it)")
     ap.add_argument("--cpu-procs", type=int, default=None,
