@@ -108,3 +108,90 @@ def test_noalloc_step_rejects_a_step_beyond_its_scratch():
     torch.cuda.synchronize()
     for t in got.values():
         assert bool((t == 7.0).all())
+
+
+def _graph_replays_match(call, outs, refs, eager_work, reps=4):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        for t in outs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in refs:
+            assert torch.equal(outs[k], refs[k]), f"replay {rep}: {k} differs"
+        eager_work()
+        torch.cuda.synchronize()
+
+
+def test_noalloc_step_under_graph_capture():
+    """The callers it is for may capture it in a HIP graph: every replay, with
+    eager calls on the same scratch in between, gives cpdec_cp_decode's bits."""
+    _say("noalloc step, HIP graph replay")
+    for w in (sc.WORKLOADS["c2"], sc.small("c4", B=2, Lcap=512)):
+        inp = sg.attn_inputs(w)
+        ref = _outputs(w, inp["q"].dtype)
+        _run(cp.StepCall, inp, ref)
+        outs = _outputs(w, inp["q"].dtype)
+        call = cp.StepCallNoAlloc(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"],
+                                  outs["o_part"], outs["lse_part"], outs["out"], outs["lse_out"])
+        scratch_outs = _outputs(w, inp["q"].dtype)
+        _graph_replays_match(call, outs, ref,
+                             lambda: _run(cp.StepCallNoAlloc, inp, scratch_outs))
+        for k in ref:
+            assert torch.equal(scratch_outs[k], ref[k]), k
+
+
+FIRST_CALL_UNDER_CAPTURE = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import torch
+import lse_merge_split_amd as cp
+from synth import configs as sc, gpu as sg
+torch.cuda.set_device(0)
+w = sc.WORKLOADS["c2"]
+inp = sg.attn_inputs(w)
+mk = lambda: [torch.empty((w.R, w.B, w.Hq, w.D), dtype=torch.float32, device="cuda"),
+              torch.empty((w.R, w.B, w.Hq), dtype=torch.float32, device="cuda"),
+              torch.empty((w.B, w.Hq, w.D), dtype=inp["q"].dtype, device="cuda"),
+              torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")]
+ref = mk()
+cp.cp_decode(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], *ref)
+got = mk()
+call = cp.StepCallNoAlloc(inp["q"], inp["k_shards"], inp["v_shards"], inp["lens"], *got)
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(side):
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream().cuda_stream)
+for rep in range(3):
+    for t in got:
+        t.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep} differs"
+print("first call under capture ok", flush=True)
+"""
+
+
+def test_noalloc_first_call_of_a_process_under_graph_capture():
+    """A fresh process whose very first cpdec_cp_decode_noalloc call is made
+    under graph capture (the scratch lookup and its counter clear happen
+    then): the replays give cpdec_cp_decode's bits."""
+    import os
+    import subprocess
+    _say("noalloc step, first call of a process under capture")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", FIRST_CALL_UNDER_CAPTURE, root], capture_output=True,
+                       text=True, timeout=180)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert "first call under capture ok" in r.stdout
