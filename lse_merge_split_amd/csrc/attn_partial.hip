@@ -167,6 +167,25 @@ __device__ __forceinline__ f32x4 load4_dev(rsrc_t r, uint32_t off, int odt) {
   return f32x4{f16_lo(w[0]), f16_hi(w[0]), f16_lo(w[1]), f16_hi(w[1])};
 }
 
+// load4_dev in two halves with no branch between the load and the loads
+// issued before it: both widths are requested, the one `odt` does not use at
+// an out-of-range offset (no memory traffic), and raw4_f32 converts where the
+// value is used.  (A branch around a load makes the compiler wait for every
+// outstanding load where the paths join.)
+struct Raw4 {
+  u32x4 w4;
+  u32x2 w2;
+};
+__device__ __forceinline__ Raw4 load4_dev_raw(rsrc_t r, uint32_t off, int odt) {
+  const bool f32 = odt == kF32;
+  return Raw4{ld16_dev(r, f32 ? off : kOutOfRange), ld8_dev(r, f32 ? kOutOfRange : off)};
+}
+__device__ __forceinline__ f32x4 raw4_f32(const Raw4& x, int odt) {
+  if (odt == kF32) return __builtin_bit_cast(f32x4, x.w4);
+  if (odt == kBF16) return f32x4{bf16_lo(x.w2[0]), bf16_hi(x.w2[0]), bf16_lo(x.w2[1]), bf16_hi(x.w2[1])};
+  return f32x4{f16_lo(x.w2[0]), f16_hi(x.w2[0]), f16_lo(x.w2[1]), f16_hi(x.w2[1])};
+}
+
 // The values x takes once stored as dtype `odt`.
 __device__ __forceinline__ f32x4 round4(f32x4 x, int odt) {
   if (odt == kBF16) {
@@ -713,9 +732,9 @@ __device__ void merge_shards(const Args& p, int b, int h, int gb, const int* s_n
     const int r = t / ng;
     l_first = ld4f_dev(l_rs, s_nl[r] > 0 ? (uint32_t)((r * rstride + row0 + t % ng) * 4) : kOutOfRange);
   }
-  f32x4 pre[RB];  // shards 0..RB-1 of output vector e = t
+  Raw4 pre[RB];  // shards 0..RB-1 of output vector e = t
 #pragma unroll
-  for (int j = 0; j < RB; ++j) pre[j] = load4_dev(o_rs, vec_off(j, t), p.odt);
+  for (int j = 0; j < RB; ++j) pre[j] = load4_dev_raw(o_rs, vec_off(j, t), p.odt);
 
   if (t < R * ng) ms.lse[t] = s_nl[t / ng] > 0 ? l_first : neg_inf();
   for (int i = t + NT; i < R * ng; i += NT) {
@@ -746,7 +765,7 @@ __device__ void merge_shards(const Args& p, int b, int h, int gb, const int* s_n
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
         const float w = j < R ? (float)ms.ew[min(j, R - 1) * ng + g] : 0.f;
-        acc += w * pre[j];
+        acc += w * raw4_f32(pre[j], p.odt);
       }
       store4(p.out, row * D + 4 * qd, acc * (float)(1.0 / S), p.out_dt);
       if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (float)((double)ms.M[g] + log(S));
@@ -828,7 +847,7 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
           f32x4, ld16_dev(wo_rs, (nl_first >= 2 && cc < nl_first) ? base + cc * cstride : kOutOfRange));
     }
   }
-  const f32x4 pre_one = load4_dev(
+  const Raw4 pre_one = load4_dev_raw(
       o_rs,
       (nl_first == 1 && part_id == 0)
           ? (uint32_t)(((r_first * rstride + row0 + e_first / Q) * D + 4 * (e_first % Q)) * es)
@@ -938,7 +957,7 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
           }
         }
       } else if (nl == 1 && part_id == 0) {
-        y = i0 == 0 ? pre_one
+        y = i0 == 0 ? raw4_f32(pre_one, p.odt)
                     : load4_dev(o_rs, (uint32_t)(((r * rstride + row0 + e / Q) * D + 4 * (e % Q)) * es),
                                 p.odt);
       }
@@ -975,9 +994,10 @@ __device__ void merge_chunks(const Args& p, int b, int h, int gb, const int* s_n
 // shuffle trees' summation order, except that the cross-shard weights that
 // scale the output are FP32 here (the output moves by ~1e-7 of itself, far
 // inside its tolerance) so that the FP64 merged lse can be formed beside the
-// output instead of ahead of it.  KB chunk vectors are loaded per thread
-// group.  Needs R * Q <= threads and every live chunk among the KB * P a
-// thread group loads (both hold where it is called).
+// output instead of ahead of it, and that the FP32 statistics take exp, log
+// and 1/x from the hardware instructions (about 1 ulp each).  KB chunk
+// vectors are loaded per thread group.  Needs R * Q <= threads and every live
+// chunk among the KB * P a thread group loads (both hold where it is called).
 template <int D, int NW, int MODE, int KB = 16>
 __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, const int* s_nl,
                                  MergeSmem<NW, MODE>& ms, int lg_nchp) {
@@ -1029,30 +1049,39 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
           f32x4, ld16_dev(wo_rs, (nli >= 2 && cc < nli) ? base + (uint32_t)cc * cstride : kOutOfRange));
     }
   }
-  const f32x4 v_one = load4_dev(
+  const Raw4 v_one = load4_dev_raw(
       o_rs, (nli == 1 && part == 0) ? (uint32_t)(((ri * rstride + row0) * D + 4 * qi) * es) : kOutOfRange,
       p.odt);
 
   // ---- (1)+(2) wave 0: chunk weights, shard lse, cross-shard weights ----
+  // The global stores (split shards' lse_part and o_part) are issued after the
+  // last barrier: a workgroup barrier waits for this wave's outstanding
+  // stores too, which would put a store round trip on the path to the output.
+  float ls_split = 0.f;  // lse_part of a split shard, stored by lane cl == 0
   if (t < 64) {
     const float lv = chunk_l ? lc : shard_l ? ls1 : neg_inf();
-    const float M = lane_reduce(lv, lg_nchp, OpMax{});     // over the shard's lanes
-    const float e = M == neg_inf() ? 0.f : expf(lv - M);  // -inf chunks give 0
+    // This chain is the merge's critical path, a few hundred dependent
+    // instructions: exp, log and reciprocal use the hardware's base-2
+    // exponential, logarithm and reciprocal (about 1 ulp each, against the
+    // library calls' dozen instructions apiece).
+    const float M = lane_reduce(lv, lg_nchp, OpMax{});       // over the shard's lanes
+    const float e = M == neg_inf() ? 0.f : __expf(lv - M);  // -inf chunks give 0
     const float S = lane_reduce(e, lg_nchp, OpSum{});
-    if (nll >= 2 && cl < nll) ms.w[rl * nch + cl] = e * (1.0f / S);
-    const float ls = S > 0.f ? M + logf(S) : neg_inf();  // shard lse (nl == 1: the stored one)
-    if (nll >= 2 && cl == 0) p.lse_part[rl * rstride + row0] = ls;
+    if (nll >= 2 && cl < nll) ms.w[rl * nch + cl] = e * __builtin_amdgcn_rcpf(S);
+    // shard lse (nl == 1: the stored one, S = 1)
+    const float ls = S > 0.f ? M + __builtin_amdgcn_logf(S) * kLn2 : neg_inf();
+    ls_split = ls;
     const float Mx = wave_max(cl == 0 ? ls : neg_inf());  // max over shards
     // FP32 cross-shard weights for the output; the merged lse is formed in
     // FP64 at the end, off the path to the output.
-    const float ew = (cl == 0 && rl < R && ls != neg_inf()) ? expf(ls - Mx) : 0.f;
+    const float ew = (cl == 0 && rl < R && ls != neg_inf()) ? __expf(ls - Mx) : 0.f;
     const float St = wave_sum(ew);
     if (cl == 0 && rl < R) {
       ms.lse[rl] = ew;               // shard weight (unnormalised)
       ms.lse[kMaxShards + rl] = ls;  // shard lse, for the merged lse
     }
     if (lane == 0) {
-      ms.M[0] = St > 0.f ? 1.0f / St : 0.f;
+      ms.M[0] = St > 0.f ? __builtin_amdgcn_rcpf(St) : 0.f;
       ms.M[1] = Mx;
     }
   }
@@ -1074,7 +1103,7 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
 #pragma unroll
       for (int k = 0; k < 4; ++k) y[k] = live ? yj[k] : y[k];
     }
-    if (nli == 1) y = v_one;
+    if (nli == 1) y = raw4_f32(v_one, p.odt);
   }
   if (P > 1) {
     ms.part[t] = y;
@@ -1082,13 +1111,8 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
     if (part == 0)
       for (int q = 1; q < P; ++q) y += ms.part[t + q * per];
   }
-  if (part == 0 && ri < R) {
-    if (nli >= 2) {
-      store4(p.o_part, (int64_t)(ri * rstride + row0) * D + 4 * qi, y, p.odt);
-      y = round4(y, p.odt);
-    }
-    ms.y[it] = y;
-  }
+  const f32x4 y_split = y;  // o_part of a split shard, stored at the end
+  if (part == 0 && ri < R) ms.y[it] = nli >= 2 ? round4(y, p.odt) : y;
   __syncthreads();
 
   // ---- (4) cross-shard merge, shard order ----
@@ -1111,6 +1135,10 @@ __device__ void merge_row_chunks(const Args& p, int b, int h, int gb, int g, con
     const double St = wave_sum_f64(e);
     if (r == 0) p.lse_out[row0] = St > 0.0 ? (float)((double)Mx + log(St)) : neg_inf();
   }
+  // ---- split shards' partials (no barrier follows) ----
+  if (part == 0 && ri < R && nli >= 2)
+    store4(p.o_part, (int64_t)(ri * rstride + row0) * D + 4 * qi, y_split, p.odt);
+  if (t < 64 && nll >= 2 && cl == 0) p.lse_part[rl * rstride + row0] = ls_split;
 }
 
 
