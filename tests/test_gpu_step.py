@@ -210,9 +210,11 @@ def test_step_padding_is_never_read():
 def test_step_16bit_partials(o_dt):
     """o_part stored in 16 bits: the merged output meets the bar against the
     storage-aware oracle (exact partials rounded to the storage type, then
-    merged exactly), in the one-launch split, two-level and unsplit forms and
-    the attention + row-merge form."""
+    merged exactly), in the one-launch split, two-level, single-head and
+    unsplit forms and the attention + row-merge form."""
     for name, w, launches in (("split", sc.small("c4", B=2, Hq=16, Lcap=512), 1),
+                              ("split, single head", sc.small("c4", B=2, Hq=8, Hkv=8, Lcap=512), 1),
+                              ("split, single head, c1 shape", sc.WORKLOADS["c1"], 1),
                               ("split, two levels", sc.small("c4", B=2, Hq=32, Lcap=512), 1),
                               ("split, attention + row merge", sc.small("c4", B=2, Lcap=512), 2),
                               ("unsplit", sc.small("c4", B=16, Lcap=512), 1)):
