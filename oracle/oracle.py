@@ -22,7 +22,7 @@ Source of the method (cited by page title and section):
     divides by a denominator; the fused kernel computes LSE-based softmax
     weights, accumulates in FP32 and converts to FP16/BF16.
 
-Readings where the page is silent (each is listed in the design doc):
+Readings where the page is silent:
   * lse is a natural logarithm; softmax scale 1/sqrt(D) unless given.
   * GQA: query head hq reads kv head hq // (Hq / Hkv).
   * weights = exp(lse_r - max_r lse_r) and denominator = sum of weights.
